@@ -1,0 +1,183 @@
+"""Decode-step benchmark: append + paged decode attention on one MI355X.
+
+A step is one pass of the decode hot path over one batch of synthetic input
+already resident in HBM: kv_append_paged (this step's K/V rows into their
+slots), the split-KV partials kernel and the log-sum-exp merge kernel.  The
+default workload is the Llama-3-8B-shaped GQA batch (H_q = 32, H_kv = 8,
+d_head = 128, batch 64, lengths uniform in [512, 8192], bf16, 16-token blocks
+randomly placed).
+
+Prints ONE JSON line.  ``value`` is KV GB/s: the K and V bytes of every
+visible position (the algorithmic bytes of the step) divided by the measured
+time per step.  The line also carries decode-attention tokens/s (sequences
+per second for one layer call), the roofline of the dominant kernel (the
+partials kernel, timed with HIP events around each of its launches on the
+launch stream), and the fp64 CPU oracle timed on a bounded sample of the
+same workload on this host (a reported baseline, not the target).
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attn KV GB/s (% of HBM peak) + tokens/s, GQA 8:1 paged, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_llama3_8b",
+                    choices=["gqa_llama3_8b", "mha_llama2_7b", "long_gqa_split", "tiny"])
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="partition tokens (-1: the workload's own, 0: library auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def up(a, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def cpu_baseline(inp, target_s):
+    """Time the fp64 oracle on whole sequences of the workload until ~target_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    t0 = time.perf_counter()
+    done = 0
+    tokens = 0
+    order = np.random.default_rng(0).permutation(inp.B)
+    for b in order:
+        sl = slice(int(b), int(b) + 1)
+        oracle.decode_attn_paged(inp.q[sl], inp.k_pool, inp.v_pool, inp.block_table[sl],
+                                 inp.seq_lens[sl], inp.dtype, inp.k_new[sl], inp.v_new[sl])
+        done += 1
+        tokens += int(inp.seq_lens[b])
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    elem = 2 if inp.dtype == "bf16" else 4
+    kv_bytes = 2 * tokens * inp.H_kv * inp.d * elem
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {inp.B} sequences ({tokens} positions, all heads) in "
+                      f"{dt:.1f} s; fp64 numpy on {os.cpu_count()} host CPUs",
+            "tokens_per_s": done / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_decode_02_amd as kvd
+    from workloads import make_config_inputs, config
+
+    cfg = config(args.workload)
+    dev = torch.device("cuda:0")
+    inp = make_config_inputs(args.workload, sentinel="zero")[0]
+    pt = cfg["partition"] if args.partition < 0 else args.partition
+    q, kc, vc = up(inp.q, dev), up(inp.k_pool, dev), up(inp.v_pool, dev)
+    kn, vn = up(inp.k_new, dev), up(inp.v_new, dev)
+    table, seq = up(inp.block_table, dev), up(inp.seq_lens, dev)
+    H_q, H_kv, d, L = inp.H_q, inp.H_kv, inp.d, inp.max_seq_len
+    pt_used = kvd.decode_attn_partition_tokens(inp.B, H_q, H_kv, d, L, pt)
+    ws = kvd.alloc_workspace(inp.B, H_q, H_kv, d, L, pt)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        kvd.kv_append_paged(kc, vc, kn, vn, table, seq)
+        if ev is not None:
+            ev[0].record(stream)
+        kvd.decode_attn_paged_partials(q, kc, vc, table, seq, L, ws, partition_tokens=pt)
+        if ev is not None:
+            ev[1].record(stream)
+        kvd.decode_attn_merge(out, seq, H_kv, L, ws, partition_tokens=pt)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_avg = float(np.mean(part_ms))
+
+    kv_bytes = inp.kv_bytes_read
+    step_s = ms_step / 1e3
+    value = kv_bytes / step_s / 1e9
+    achieved = kv_bytes / (part_avg / 1e3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": H_q,
+                   "num_kv_heads": H_kv, "head_dim": d, "block_size": 16,
+                   "sum_seq_len": int(inp.seq_lens.astype(np.int64).sum()),
+                   "max_seq_len": L, "partition_tokens": pt_used},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(inp.B / step_s, 1),
+        "kv_bytes_per_step": kv_bytes,
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {"partials_avg": round(part_avg, 5), "partials_min": round(min(part_ms), 5),
+                      "partials_max": round(max(part_ms), 5)},
+        "roofline": {"bound": "hbm", "kernel": "paged_partials_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

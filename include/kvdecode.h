@@ -1,0 +1,181 @@
+/*
+ * kvdecode.h -- C ABI of the paged decode-attention library (gfx950 / MI355X).
+ *
+ * One decode step of one attention layer is two calls: append this step's
+ * K/V row into the paged cache, then attend over the whole visible history
+ * with the step's query ("append, then read all history": LLM Compass
+ * "KV Cache（键值缓存）", section 4 实现要点, the decode_step sketch; LLM
+ * Systems Wiki "KV缓存原理与显存估算", 知识点二).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every tensor pointer is DEVICE memory owned by the caller.  The
+ *   library allocates nothing, frees nothing, keeps no state between calls
+ *   and never writes q, k_new, v_new, c_new, block_table or seq_lens.
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Calls only enqueue work: a return of KVD_OK means "validated
+ *   and launched", not "finished".  Calls on one stream run in order.
+ * Errors: arguments are checked on the host before anything is launched; a
+ *   negative status is returned and nothing is enqueued.  The checks read no
+ *   device memory, so contents (seq_lens, table entries) are preconditions:
+ *     1 <= seq_lens[b] <= min(max_seq_len, max_blocks_per_seq * block_size);
+ *     table entries of the blocks that hold positions < seq_lens[b] lie in
+ *     [0, num_blocks); the block receiving an appended row is owned by that
+ *     sequence alone (shared prefix blocks are copy-on-write: "KV Cache（键值
+ *     缓存）", 2.3 路线二); inputs are finite.
+ *   The kernels never read or write outside the buffers described here even
+ *   when these are violated: lengths are clamped to the table row, and a
+ *   table entry outside [0, num_blocks) is skipped (its tokens contribute
+ *   nothing and no append is made to it).  A sequence with seq_lens[b] <= 0
+ *   gets an all-zero output row.
+ * Layouts (row-major, innermost last):
+ *   paged K or V cache   [num_blocks, block_size, num_kv_heads, head_dim]
+ *       token-major inside a block, the per-token [seq, heads, d_head]
+ *       layout of the "单请求 KV Cache" tutorial (past_key_values 的数据结构);
+ *       with an identity block table it is exactly that contiguous cache.
+ *   block_table          int32 [batch, max_blocks_per_seq]: row b maps
+ *       logical block j (positions 16j .. 16j+15) of sequence b to a physical
+ *       block ("KV-Cache——为什么AI回复越来越快", 08 PagedAttention（vLLM）).
+ *   seq_lens             int32 [batch]: length of sequence b AFTER this
+ *       step's append, so the new row lands at position seq_lens[b] - 1
+ *       ("KV缓存原理与显存估算", 前置知识: cache length counts the positions
+ *       already forwarded).
+ *   q, out               [batch, num_q_heads, head_dim]; query head h reads
+ *       K/V head h / (num_q_heads / num_kv_heads) (contiguous groups: "KV-
+ *       Cache——为什么AI回复越来越快", 03 三种Attention架构, GQA).
+ * Types: KVD_BF16 tensors hold bfloat16, KVD_F32 tensors hold float.  The
+ *   output has q's type; bf16 outputs are rounded to nearest even.  All
+ *   arithmetic is fp32.
+ */
+#ifndef KVDECODE_H
+#define KVDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KVD_F32 = 0, KVD_BF16 = 1 } kvd_dtype_t;
+
+enum {
+    KVD_OK = 0,
+    KVD_ERR_NULL = -1,        /* a required pointer is NULL */
+    KVD_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
+    KVD_ERR_UNSUPPORTED = -3, /* dtype, head_dim, block_size or head ratio not built */
+    KVD_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required */
+    KVD_ERR_HIP = -5          /* the HIP runtime reported a launch error */
+};
+
+/* Static English text for a status code (never NULL). */
+const char* kvd_status_string(int status);
+
+/*
+ * kv_append_paged -- write this step's K/V rows into their cache slots.
+ *
+ * For each sequence b: pos = seq_lens[b] - 1, blk = block_table[b][pos / 16],
+ * off = pos % 16; then K[blk][off][:][:] = k_new[b] and V[blk][off][:][:] =
+ * v_new[b], an in-place O(1) slot write instead of re-concatenating the
+ * history ("单请求 KV Cache", 生产系统的做法：预分配 + in-place 写入).  The
+ * bytes are copied exactly; nothing else in the cache changes.
+ *
+ *   k_cache, v_cache  paged caches (layout above); v_cache may be NULL for a
+ *                     single latent cache (MLA), then v_new must be NULL too
+ *   k_new, v_new      [batch, num_kv_heads, head_dim] rows to store
+ *   block_table, seq_lens  as above
+ *   head_dim          any value in 1..1024 whose row size is a multiple of 4 B
+ *   block_size        must be 16
+ *   dtype             KVD_BF16 or KVD_F32
+ * Returns KVD_OK or a negative status (nothing enqueued).
+ */
+int kv_append_paged(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int batch, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int num_blocks, kvd_dtype_t dtype, void* stream);
+
+/*
+ * decode_attn_partition_tokens -- the KV partition size (tokens) that the
+ * decode calls will use for these sizes: `partition_tokens` itself when it is
+ * positive (it must then be a multiple of 16), otherwise the library's
+ * automatic choice.  Returns a negative status for invalid sizes.
+ */
+int decode_attn_partition_tokens(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_seq_len, int partition_tokens);
+
+/*
+ * decode_attn_workspace_bytes -- bytes of device workspace a decode call
+ * needs (fp32 partial results of every KV partition).  For MLA pass
+ * num_kv_heads = 1 and head_dim = d_c.  Returns 0 for invalid sizes.
+ */
+size_t decode_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int max_seq_len, int partition_tokens);
+
+/*
+ * decode_attn_paged -- single-query decode attention over a paged cache.
+ *
+ * For each sequence b and query head h, with g = h / (num_q_heads /
+ * num_kv_heads) and L = seq_lens[b]:
+ *   z_t = scale * q[b][h] . K_b[t][g]          for t in [0, L)
+ *   out[b][h] = sum_t softmax(z)_t V_b[t][g]
+ * where K_b[t] is the row at block_table[b][t / 16], offset t % 16 ("KV缓存原
+ * 理与显存估算", 知识点二, the z / a / o equations; "KV-Cache——为什么AI回复越
+ * 来越快", 02, the decode-step Attention(Q_{p+t}, K_cache, V_cache)).  All L
+ * positions are visible: a single decode row has nothing in its future
+ * ("单请求 KV Cache", 改动三).
+ *
+ * Implementation: positions are cut into partitions of
+ * decode_attn_partition_tokens(...) tokens; a first kernel writes each
+ * partition's running max, sum and unnormalised output into `workspace`, a
+ * second merges the partitions by log-sum-exp into `out`.  The two phases are
+ * also exported separately below.
+ *
+ *   out              [batch, num_q_heads, head_dim], dtype
+ *   q                [batch, num_q_heads, head_dim], dtype
+ *   k_cache, v_cache [num_blocks, 16, num_kv_heads, head_dim], dtype
+ *   head_dim         32, 64 or 128
+ *   num_q_heads      a multiple of num_kv_heads; the ratio 1, 2, 4, 8 or a
+ *                    multiple of 8 up to 64
+ *   max_seq_len      host-known upper bound of seq_lens (sizes the grid)
+ *   scale            score scale, normally 1/sqrt(head_dim)
+ *   partition_tokens 0 for automatic, else a multiple of 16
+ *   workspace        >= decode_attn_workspace_bytes(...) bytes, 256-B aligned
+ */
+int decode_attn_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int num_blocks,
+                      int max_seq_len, float scale, int partition_tokens,
+                      void* workspace, size_t workspace_bytes, kvd_dtype_t dtype, void* stream);
+
+/*
+ * decode_attn_paged_partials -- first phase of decode_attn_paged only: fills
+ * `workspace` with every partition's partial results.  Same arguments minus
+ * `out`.  The workspace format is private to the library; pass it unchanged
+ * to decode_attn_merge with the same sizes.
+ */
+int decode_attn_paged_partials(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               int max_seq_len, float scale, int partition_tokens,
+                               void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                               void* stream);
+
+/*
+ * decode_attn_merge -- second phase: for each (b, h), with M the largest
+ * partition maximum, out = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p
+ * over the partitions that hold positions of sequence b.  Sizes must equal
+ * those of the partials call that filled `workspace` (for MLA: num_kv_heads =
+ * 1, head_dim = d_c).
+ */
+int decode_attn_merge(void* out, const int32_t* seq_lens, int batch, int num_q_heads,
+                      int num_kv_heads, int head_dim, int max_seq_len, int partition_tokens,
+                      const void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDECODE_H */

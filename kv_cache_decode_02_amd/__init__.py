@@ -1,0 +1,27 @@
+"""Paged decode attention for MI355X (gfx950): Python face of libkvdecode.so.
+
+One decode step of one layer: ``kv_append_paged`` writes the step's K/V row
+into the paged cache, ``decode_attn_paged`` attends over the whole visible
+history (split-KV partials, then a log-sum-exp merge).  The functions mirror
+the C ABI in ``include/kvdecode.h`` and only marshal arguments; importing this
+package fails if the HIP library has not been built.
+"""
+
+from ._native import (
+    KvdError,
+    kv_append_paged,
+    decode_attn_paged,
+    decode_attn_paged_partials,
+    decode_attn_merge,
+    decode_attn_workspace_bytes,
+    decode_attn_partition_tokens,
+    alloc_workspace,
+    LIB_PATH,
+    HEADER_PATH,
+)
+
+__all__ = [
+    "KvdError", "kv_append_paged", "decode_attn_paged", "decode_attn_paged_partials",
+    "decode_attn_merge", "decode_attn_workspace_bytes", "decode_attn_partition_tokens",
+    "alloc_workspace", "LIB_PATH", "HEADER_PATH",
+]

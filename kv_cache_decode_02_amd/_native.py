@@ -1,0 +1,193 @@
+"""ctypes binding of libkvdecode.so: argument marshalling only.
+
+Every computation happens in the HIP library; this module turns torch tensors
+into device pointers and sizes, passes torch's current HIP stream, and maps
+negative status codes to exceptions (ValueError for argument errors,
+RuntimeError for HIP runtime errors).  Importing it fails loudly when the
+library has not been built.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kvdecode.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m kv_cache_decode_02_amd.build or __graft_entry__.build())")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+KVD_F32 = 0
+KVD_BF16 = 1
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_f = ctypes.c_float
+
+lib.kvd_status_string.restype = ctypes.c_char_p
+lib.kvd_status_string.argtypes = [_i]
+lib.kv_append_paged.restype = _i
+lib.kv_append_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
+lib.decode_attn_partition_tokens.restype = _i
+lib.decode_attn_partition_tokens.argtypes = [_i, _i, _i, _i, _i, _i]
+lib.decode_attn_workspace_bytes.restype = _sz
+lib.decode_attn_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+_PAGED_ARGS = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]
+lib.decode_attn_paged.restype = _i
+lib.decode_attn_paged.argtypes = [_vp] + _PAGED_ARGS
+lib.decode_attn_paged_partials.restype = _i
+lib.decode_attn_paged_partials.argtypes = _PAGED_ARGS
+lib.decode_attn_merge.restype = _i
+lib.decode_attn_merge.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]
+
+
+class KvdError(ValueError):
+    """An argument was rejected by the library's host-side checks."""
+
+
+def _check(status, what):
+    if status == 0:
+        return
+    msg = f"{what}: {lib.kvd_status_string(status).decode()} (status {status})"
+    if status == -5:
+        raise RuntimeError(msg)
+    raise KvdError(msg)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KVD_BF16
+    if t.dtype == torch.float32:
+        return KVD_F32
+    raise KvdError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, device=True, dtype=None, contiguous=True):
+    if t is None:
+        raise KvdError(f"{name} is required")
+    if device and not t.is_cuda:
+        raise KvdError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise KvdError(f"{name} must be {dtype}")
+    if contiguous and not t.is_contiguous():
+        raise KvdError(f"{name} must be contiguous")
+
+
+def kv_append_paged(k_cache, v_cache, k_new, v_new, block_table, seq_lens, stream=None):
+    """Write each sequence's new row at position seq_lens[b] - 1 of its cache.
+
+    k_cache/v_cache: [num_blocks, 16, H_kv, d]; k_new/v_new: [B, H_kv, d];
+    v_cache and v_new may both be None (latent cache).
+    """
+    for t, n in ((k_cache, "k_cache"), (k_new, "k_new"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens")):
+        _need(t, n)
+    _need(block_table, "block_table", dtype=torch.int32)
+    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    nb, bs, h_kv, d = k_cache.shape
+    B = k_new.shape[0]
+    status = lib.kv_append_paged(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                 _ptr(block_table), _ptr(seq_lens), B, h_kv, d, bs,
+                                 block_table.shape[1], nb, _dtype_code(k_cache), _stream(stream))
+    _check(status, "kv_append_paged")
+
+
+def decode_attn_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                 partition_tokens=0):
+    r = lib.decode_attn_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim,
+                                         max_seq_len, partition_tokens)
+    _check(min(r, 0), "decode_attn_partition_tokens")
+    return r
+
+
+def decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                partition_tokens=0):
+    n = lib.decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                        max_seq_len, partition_tokens)
+    if n == 0:
+        raise KvdError("decode_attn_workspace_bytes: invalid sizes")
+    return n
+
+
+def alloc_workspace(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens=0,
+              device="cuda"):
+    """A device buffer of the size the decode calls need (torch allocation)."""
+    n = decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                    partition_tokens)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+                partition_tokens, ws):
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_table, "block_table"), (seq_lens, "seq_lens"), (ws, "workspace")):
+        _need(t, n)
+    _need(block_table, "block_table", dtype=torch.int32)
+    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    B, h_q, d = q.shape
+    nb, bs, h_kv, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise KvdError("q, k_cache and v_cache head sizes disagree")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise KvdError("q, k_cache and v_cache must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+            B, h_q, h_kv, d, bs, block_table.shape[1], nb, int(max_seq_len), float(scale),
+            int(partition_tokens), _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q)]
+
+
+def decode_attn_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=None,
+                      partition_tokens=0, workspace=None, out=None, stream=None):
+    """Decode attention of q [B, H_q, d] over the paged K/V caches; returns out."""
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    if workspace is None:
+        workspace = alloc_workspace(B, h_q, h_kv, d, max_seq_len, partition_tokens,
+                                    device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype)
+    args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+                       partition_tokens, workspace)
+    _check(lib.decode_attn_paged(_ptr(out), *args, _stream(stream)), "decode_attn_paged")
+    return out
+
+
+def decode_attn_paged_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
+                               workspace, scale=None, partition_tokens=0, stream=None):
+    """First phase only: fills ``workspace`` with per-partition partials."""
+    args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+                       partition_tokens, workspace)
+    _check(lib.decode_attn_paged_partials(*args, _stream(stream)), "decode_attn_paged_partials")
+
+
+def decode_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_tokens=0,
+                      stream=None):
+    """Second phase only: merges the partials in ``workspace`` into ``out``."""
+    _need(out, "out")
+    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    _need(workspace, "workspace")
+    B, h_q, d = out.shape
+    status = lib.decode_attn_merge(_ptr(out), _ptr(seq_lens), B, h_q, num_kv_heads, d,
+                                   int(max_seq_len), int(partition_tokens), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _dtype_code(out), _stream(stream))
+    _check(status, "decode_attn_merge")

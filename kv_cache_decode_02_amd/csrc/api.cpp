@@ -1,0 +1,296 @@
+// C ABI of the decode library: host-side argument checks, partition choice
+// and kernel dispatch.  Every check below runs before any HIP call, reads no
+// device memory and allocates nothing.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/kvdecode.h"
+#include "kvd_internal.h"
+
+namespace kvd {
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr int kMinPartition = 64;
+constexpr int kMaxPartition = 1024;   // 64 blocks: one block id per lane
+constexpr long long kTargetWaves = 16384;
+constexpr int kMaxTableBlocks = 1 << 26;  // keeps max_blocks_per_seq * 16 in int
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int heads_per_wave(int ratio) { return ratio < 8 ? ratio : 8; }
+
+bool dtype_ok(int dtype) { return dtype == KVD_F32 || dtype == KVD_BF16; }
+
+int elem_bytes(int dtype) { return dtype == KVD_BF16 ? 2 : 4; }
+
+int check_heads(int batch, int num_q_heads, int num_kv_heads) {
+  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1) return KVD_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return KVD_ERR_SHAPE;
+  return KVD_OK;
+}
+
+// Partition size: the given one, or the largest of 1024 .. 64 that still
+// gives at least kTargetWaves wavefronts for a batch at max_seq_len.
+int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int max_seq_len,
+                      int partition_tokens) {
+  if (partition_tokens > 0) {
+    if (partition_tokens % kBlockSize != 0 || partition_tokens > kMaxPartition) return KVD_ERR_SHAPE;
+    return partition_tokens;
+  }
+  if (partition_tokens < 0) return KVD_ERR_SHAPE;
+  const int ratio = num_q_heads / num_kv_heads;
+  const long long units = static_cast<long long>(batch) * num_kv_heads * (ratio / heads_per_wave(ratio));
+  int pt = kMaxPartition;
+  while (pt > kMinPartition) {
+    const long long parts = (max_seq_len + pt - 1) / pt;
+    if (units * parts >= kTargetWaves) break;
+    pt /= 2;
+  }
+  return pt;
+}
+
+struct Sizes {
+  int pt;
+  int parts;
+  WorkspaceLayout ws;
+};
+
+int plan(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
+         int partition_tokens, Sizes* s) {
+  int rc = check_heads(batch, num_q_heads, num_kv_heads);
+  if (rc) return rc;
+  if (head_dim < 1 || max_seq_len < 1) return KVD_ERR_SHAPE;
+  const int pt = resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
+  if (pt < 0) return pt;
+  s->pt = pt;
+  s->parts = (max_seq_len + pt - 1) / pt;
+  // The grid and the workspace must stay addressable.
+  const long long ratio = num_q_heads / num_kv_heads;
+  const long long waves = static_cast<long long>(batch) * s->parts * num_kv_heads *
+                          (ratio / heads_per_wave(static_cast<int>(ratio)));
+  if (waves >= INT_MAX || static_cast<long long>(batch) * num_q_heads >= INT_MAX / 4)
+    return KVD_ERR_SHAPE;
+  s->ws = workspace_layout(batch, num_q_heads, s->parts, head_dim);
+  return KVD_OK;
+}
+
+int check_table(int block_size, int max_blocks_per_seq, int num_blocks, int max_seq_len) {
+  if (block_size != kBlockSize) return KVD_ERR_UNSUPPORTED;
+  if (max_blocks_per_seq < 1 || max_blocks_per_seq > kMaxTableBlocks || num_blocks < 1)
+    return KVD_ERR_SHAPE;
+  if (max_seq_len < 1 || max_seq_len > max_blocks_per_seq * kBlockSize) return KVD_ERR_SHAPE;
+  return KVD_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVD_OK : KVD_ERR_HIP; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(int batch, int num_q_heads, int num_partitions, int head_dim) {
+  WorkspaceLayout w;
+  const size_t slots = static_cast<size_t>(batch) * num_q_heads * num_partitions;
+  w.o_bytes = slots * head_dim * sizeof(float);
+  w.ml_offset = align256(w.o_bytes);
+  w.total = w.ml_offset + align256(slots * 2 * sizeof(float));
+  return w;
+}
+
+}  // namespace kvd
+
+using namespace kvd;
+
+extern "C" {
+
+const char* kvd_status_string(int status) {
+  switch (status) {
+    case KVD_OK: return "ok";
+    case KVD_ERR_NULL: return "a required pointer is NULL";
+    case KVD_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case KVD_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block_size or head ratio";
+    case KVD_ERR_WORKSPACE: return "workspace is NULL or too small";
+    case KVD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int kv_append_paged(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int batch, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int num_blocks, kvd_dtype_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return KVD_ERR_UNSUPPORTED;
+  if (batch < 0 || num_kv_heads < 1 || head_dim < 1 || head_dim > 1024) return KVD_ERR_SHAPE;
+  if (block_size != kBlockSize) return KVD_ERR_UNSUPPORTED;
+  if (max_blocks_per_seq < 1 || max_blocks_per_seq > kMaxTableBlocks || num_blocks < 1)
+    return KVD_ERR_SHAPE;
+  const long long row_bytes = static_cast<long long>(num_kv_heads) * head_dim * elem_bytes(dtype);
+  if (row_bytes % 4 != 0 || row_bytes / 4 > INT_MAX) return KVD_ERR_SHAPE;
+  if (batch == 0) return KVD_OK;  // empty batch: nothing to write, pointers unused
+  if (!k_cache || !k_new || !block_table || !seq_lens) return KVD_ERR_NULL;
+  if ((v_cache == nullptr) != (v_new == nullptr)) return KVD_ERR_NULL;
+
+  AppendLaunch a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.row_words = static_cast<int>(row_bytes / 4);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.vec16 = aligned16(k_cache) && aligned16(k_new) &&
+            (!v_cache || (aligned16(v_cache) && aligned16(v_new)));
+  return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_partition_tokens(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_seq_len, int partition_tokens) {
+  Sizes s;
+  const int rc = plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens, &s);
+  return rc ? rc : s.pt;
+}
+
+size_t decode_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int max_seq_len, int partition_tokens) {
+  Sizes s;
+  if (plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens, &s))
+    return 0;
+  return s.ws.total;
+}
+
+static int check_paged(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_blocks_per_seq, int num_blocks,
+                       int max_seq_len, int partition_tokens, const void* workspace,
+                       size_t workspace_bytes, int dtype, Sizes* s) {
+  if (!dtype_ok(dtype)) return KVD_ERR_UNSUPPORTED;
+  int rc = check_heads(batch, num_q_heads, num_kv_heads);
+  if (rc) return rc;
+  if (!paged_supported(head_dim, num_q_heads / num_kv_heads, dtype == KVD_BF16))
+    return KVD_ERR_UNSUPPORTED;
+  rc = check_table(block_size, max_blocks_per_seq, num_blocks, max_seq_len);
+  if (rc) return rc;
+  rc = plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens, s);
+  if (rc) return rc;
+  if (batch == 0) return KVD_OK;  // empty batch: nothing to compute, pointers unused
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens) return KVD_ERR_NULL;
+  if (!workspace || workspace_bytes < s->ws.total) return KVD_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return KVD_ERR_SHAPE;
+  return KVD_OK;
+}
+
+static PagedLaunch paged_launch(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                                float scale, void* workspace, int dtype, const Sizes& s) {
+  PagedLaunch a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ws.ml_offset);
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_seq_len = max_seq_len;
+  a.partition_tokens = s.pt;
+  a.num_partitions = s.parts;
+  a.scale = scale;
+  a.bf16 = dtype == KVD_BF16;
+  return a;
+}
+
+static MergeLaunch merge_launch(void* out, const int32_t* seq_lens, int batch, int num_q_heads,
+                                int head_dim, int max_seq_len, const void* workspace, int dtype,
+                                const Sizes& s) {
+  MergeLaunch m;
+  m.out = out;
+  m.seq_lens = seq_lens;
+  m.ws_o = static_cast<const float*>(workspace);
+  m.ws_ml = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + s.ws.ml_offset);
+  m.batch = batch;
+  m.num_q_heads = num_q_heads;
+  m.head_dim = head_dim;
+  m.max_blocks_per_seq_tokens = max_seq_len;
+  m.partition_tokens = s.pt;
+  m.num_partitions = s.parts;
+  m.bf16 = dtype == KVD_BF16;
+  return m;
+}
+
+int decode_attn_paged_partials(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               int max_seq_len, float scale, int partition_tokens,
+                               void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                               void* stream) {
+  Sizes s;
+  const int rc = check_paged(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                             num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                             max_seq_len, partition_tokens, workspace, workspace_bytes, dtype, &s);
+  if (rc) return rc;
+  if (batch == 0) return KVD_OK;
+  const PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch,
+                                     num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                     num_blocks, max_seq_len, scale, workspace, dtype, s);
+  return hip_status(launch_paged_partials(a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_merge(void* out, const int32_t* seq_lens, int batch, int num_q_heads,
+                      int num_kv_heads, int head_dim, int max_seq_len, int partition_tokens,
+                      const void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                      void* stream) {
+  if (!dtype_ok(dtype)) return KVD_ERR_UNSUPPORTED;
+  if (!(head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 512))
+    return KVD_ERR_UNSUPPORTED;
+  Sizes s;
+  const int rc = plan(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens, &s);
+  if (rc) return rc;
+  if (batch == 0) return KVD_OK;
+  if (!out || !seq_lens) return KVD_ERR_NULL;
+  if (!workspace || workspace_bytes < s.ws.total) return KVD_ERR_WORKSPACE;
+  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
+                                     workspace, dtype, s);
+  return hip_status(launch_merge(m, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int num_blocks,
+                      int max_seq_len, float scale, int partition_tokens,
+                      void* workspace, size_t workspace_bytes, kvd_dtype_t dtype, void* stream) {
+  Sizes s;
+  int rc = check_paged(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                       max_seq_len, partition_tokens, workspace, workspace_bytes, dtype, &s);
+  if (rc) return rc;
+  if (batch == 0) return KVD_OK;
+  if (!out) return KVD_ERR_NULL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch,
+                                     num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                     num_blocks, max_seq_len, scale, workspace, dtype, s);
+  rc = hip_status(launch_paged_partials(a, st));
+  if (rc) return rc;
+  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
+                                     workspace, dtype, s);
+  return hip_status(launch_merge(m, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Host-side interfaces between the C ABI layer (api.cpp) and the kernel
+// launchers (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace kvd {
+
+// Workspace of the split decode: per (b, h, partition) an fp32 output row of
+// head_dim values, then per (b, h, partition) the pair (max, sum).  The max is
+// kept in log2 units (scores are pre-multiplied by log2 e).
+struct WorkspaceLayout {
+  size_t o_bytes;   // [B, H_q, P, D] fp32
+  size_t ml_offset; // start of [B, H_q, P] float2, 256-B aligned
+  size_t total;
+};
+
+WorkspaceLayout workspace_layout(int batch, int num_q_heads, int num_partitions, int head_dim);
+
+struct PagedLaunch {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* ws_o;
+  float* ws_ml;
+  int batch, num_q_heads, num_kv_heads, head_dim;
+  int max_blocks_per_seq, num_blocks, max_seq_len;
+  int partition_tokens, num_partitions;
+  float scale;
+  bool bf16;
+};
+
+struct MergeLaunch {
+  void* out;
+  const int32_t* seq_lens;
+  const float* ws_o;
+  const float* ws_ml;
+  int batch, num_q_heads, head_dim;
+  int max_blocks_per_seq_tokens;  // clamp bound for seq_lens (max_seq_len)
+  int partition_tokens, num_partitions;
+  bool bf16;
+};
+
+struct AppendLaunch {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int batch, row_words;  // row_words = num_kv_heads * head_dim * elem / 4
+  int max_blocks_per_seq, num_blocks;
+  bool vec16;  // all four row buffers 16-byte aligned
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_append(const AppendLaunch& a, hipStream_t stream);
+hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream);
+hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
+
+// Whether a kernel instance exists for this head_dim / group ratio / dtype.
+bool paged_supported(int head_dim, int ratio, bool bf16);
+
+}  // namespace kvd

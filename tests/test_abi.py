@@ -1,0 +1,115 @@
+"""The C-ABI library: exports and host-side argument checks (CPU only).
+
+No call here launches a kernel: each either is pure host arithmetic
+(workspace sizing, partition choice) or is rejected by the host-side checks,
+which run before any HIP call.
+"""
+
+import ctypes
+import re
+
+import pytest
+
+import kv_cache_decode_02_amd as kvd
+from kv_cache_decode_02_amd._native import lib
+
+OK, ENULL, ESHAPE, EUNSUP, EWS = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(kvd.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "kv_append_paged" in names and "decode_attn_paged" in names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.kvd_status_string(s)
+
+
+def test_workspace_layout():
+    # P = ceil(max_len / pt) partitions; D fp32 values and (m, l) per
+    # (b, h, p), each section padded to 256 B.
+    B, Hq, Hkv, D, L, pt = 3, 8, 2, 128, 1000, 256
+    P = -(-L // pt)
+    o = B * Hq * P * D * 4
+    ml = B * Hq * P * 2 * 4
+    pad = lambda x: -(-x // 256) * 256  # noqa: E731
+    assert kvd.decode_attn_workspace_bytes(B, Hq, Hkv, D, L, pt) == pad(o) + pad(ml)
+
+
+def test_partition_choice():
+    assert kvd.decode_attn_partition_tokens(4, 64, 8, 128, 131072, 512) == 512
+    auto = kvd.decode_attn_partition_tokens(64, 32, 8, 128, 8192, 0)
+    assert auto % 16 == 0 and 64 <= auto <= 1024
+    assert kvd.decode_attn_partition_tokens(1, 4, 4, 32, 129, 0) == 64
+    with pytest.raises(kvd.KvdError):
+        kvd.decode_attn_partition_tokens(1, 4, 4, 32, 129, 24)
+    with pytest.raises(kvd.KvdError):
+        kvd.decode_attn_partition_tokens(1, 4, 4, 32, 129, 2048)
+    with pytest.raises(kvd.KvdError):
+        kvd.decode_attn_partition_tokens(1, 6, 4, 32, 129, 0)
+
+
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
+
+
+def append(**kw):
+    a = dict(k=P, v=P, kn=P, vn=P, bt=P, sl=P, B=2, hkv=8, d=128, bs=16, mb=4, nb=8, dt=1)
+    a.update(kw)
+    return lib.kv_append_paged(a["k"], a["v"], a["kn"], a["vn"], a["bt"], a["sl"], a["B"],
+                               a["hkv"], a["d"], a["bs"], a["mb"], a["nb"], a["dt"], None)
+
+
+def test_append_rejections():
+    assert append(k=None) == ENULL
+    assert append(v=None) == ENULL           # v_cache without v_new
+    assert append(bt=None) == ENULL
+    assert append(bs=32) == EUNSUP
+    assert append(dt=7) == EUNSUP
+    assert append(hkv=0) == ESHAPE
+    assert append(B=-1) == ESHAPE
+    assert append(mb=0) == ESHAPE
+    assert append(hkv=1, d=3, dt=1) == ESHAPE
+    assert append(B=0) == OK                 # empty batch: nothing to do
+
+
+def paged(**kw):
+    a = dict(o=P, q=P, k=P, v=P, bt=P, sl=P, B=2, hq=32, hkv=8, d=128, bs=16, mb=64, nb=128,
+             L=1024, scale=0.088, pt=0, ws=P, wsb=1 << 40, dt=1)
+    a.update(kw)
+    return lib.decode_attn_paged(a["o"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["B"],
+                                 a["hq"], a["hkv"], a["d"], a["bs"], a["mb"], a["nb"], a["L"],
+                                 a["scale"], a["pt"], a["ws"], a["wsb"], a["dt"], None)
+
+
+def test_decode_rejections():
+    assert paged(q=None) == ENULL
+    assert paged(o=None) == ENULL
+    assert paged(v=None) == ENULL
+    assert paged(hq=30) == ESHAPE            # not a multiple of H_kv
+    assert paged(hq=24) == EUNSUP            # ratio 3 not built
+    assert paged(d=96) == EUNSUP
+    assert paged(bs=8) == EUNSUP
+    assert paged(dt=2) == EUNSUP
+    assert paged(L=64 * 16 + 1) == ESHAPE    # beyond the table row
+    assert paged(L=0) == ESHAPE
+    assert paged(pt=40) == ESHAPE
+    assert paged(ws=None) == EWS
+    need = kvd.decode_attn_workspace_bytes(2, 32, 8, 128, 1024, 0)
+    assert paged(wsb=need - 1) == EWS
+    assert paged(B=0, ws=None, wsb=0) == OK  # empty batch: nothing to do
+
+
+def test_merge_rejections():
+    f = lib.decode_attn_merge
+    assert f(None, P, 2, 32, 8, 128, 1024, 0, P, 1 << 40, 1, None) == ENULL
+    assert f(P, P, 2, 32, 8, 96, 1024, 0, P, 1 << 40, 1, None) == EUNSUP
+    assert f(P, P, 2, 32, 8, 128, 1024, 0, P, 16, 1, None) == EWS

@@ -47,7 +47,32 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the decode step, time a plain device copy of MIB MiB "
+                         "(reference kernel for scaling HBM traffic counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib, steps, warmup):
+    """Plain copy of a known size: reads and writes exactly mib MiB per launch."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "ms_per_copy": round(ms, 5),
+                      "copy_GBps_read_plus_write": round(2 * n / (ms / 1e3) / 1e9, 1)}),
+          flush=True)
 
 
 def up(a, dev):
@@ -56,6 +81,30 @@ def up(a, dev):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     return torch.from_numpy(a).to(dev)
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None.
+
+    profiles/<kernel>__<workload>.md carries the scaled FETCH_SIZE + WRITE_SIZE
+    bytes and the SHA-256 of the kernel sources they were taken with; the
+    figure is only returned while the current sources hash the same.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    tag = "```json traffic"
+    if tag not in text:
+        return None
+    rec = json.loads(text.split(tag, 1)[1].split("```", 1)[0])
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(inp, target_s):
@@ -95,6 +144,10 @@ def main():
               "(the decode path shards by sequence or KV head with no exchange; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, args.steps, args.warmup)
+        return
 
     import torch
     import kv_cache_decode_02_amd as kvd
@@ -171,7 +224,8 @@ def main():
                       "partials_max": round(max(part_ms), 5)},
         "roofline": {"bound": "hbm", "kernel": "paged_partials_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("paged_partials", args.workload)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -121,7 +121,7 @@ def decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_
                                 partition_tokens=0):
     n = lib.decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                         max_seq_len, partition_tokens)
-    if n == 0:
+    if n == 0 and batch != 0:
         raise KvdError("decode_attn_workspace_bytes: invalid sizes")
     return n
 

@@ -14,12 +14,12 @@ namespace {
 constexpr int kBlockSize = 16;
 constexpr int kMinPartition = 64;
 constexpr int kMaxPartition = 1024;   // 64 blocks: one block id per lane
-constexpr long long kTargetWaves = 16384;
+constexpr long long kTargetWaves = 12288;
 constexpr int kMaxTableBlocks = 1 << 26;  // keeps max_blocks_per_seq * 16 in int
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-int heads_per_wave(int ratio) { return ratio < 8 ? ratio : 8; }
+int heads_per_wave(int ratio) { return ratio < 4 ? ratio : 4; }
 
 bool dtype_ok(int dtype) { return dtype == KVD_F32 || dtype == KVD_BF16; }
 

@@ -54,8 +54,18 @@ struct RowShape {
   }
 };
 
-template <bool BF16, int D, int HPW, int NBUF>
-__global__ __launch_bounds__(256) void paged_partials_kernel(PagedLaunch a) {
+// NBUF: register buffers per wave (NBUF - 1 blocks in flight during compute).
+// WPE: waves per SIMD the register allocation is sized for.
+// WG: wavefronts per workgroup.  Consecutive units are the KV heads (and head
+// chunks) of one (sequence, partition), so a workgroup's waves read the same
+// blocks together: for 8 KV heads an 8-wave workgroup reads whole contiguous
+// token rows of every block.
+// PBF16: softmax weights enter the V product as bf16 pairs (dot2, fp32
+// accumulation) instead of fp32 FMAs; only for bf16 caches.
+template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
+__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void paged_partials_kernel(PagedLaunch a) {
+  static_assert(BF16 || !PBF16, "bf16 weights need a bf16 cache");
   using S = RowShape<BF16, D>;
   constexpr int W = S::W, CW = S::CW, NCH = S::NCH, RW = S::RW, DPL = S::DPL;
 
@@ -65,7 +75,7 @@ __global__ __launch_bounds__(256) void paged_partials_kernel(PagedLaunch a) {
   const int ratio = a.num_q_heads / a.num_kv_heads;
   const int hchunks = ratio / HPW;
 
-  int u = wave_uniform(blockIdx.x * 4 + (threadIdx.x >> 6));
+  int u = wave_uniform(blockIdx.x * WG + (threadIdx.x >> 6));
   const int units = a.batch * a.num_partitions * a.num_kv_heads * hchunks;
   if (u >= units) return;
   const int hc = u % hchunks;
@@ -107,10 +117,17 @@ __global__ __launch_bounds__(256) void paged_partials_kernel(PagedLaunch a) {
     for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
   }
 
-  const uint32_t* kbase = static_cast<const uint32_t*>(a.k_cache) + g * RW;
-  const uint32_t* vbase = static_cast<const uint32_t*>(a.v_cache) + g * RW;
-  const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * RW;
+  const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * RW;  // words per token
   const float sl2 = a.scale * kLog2e;
+  // Byte offset, inside a physical block, of the lane's chunk 0 for its two
+  // token slots (tokens grp and grp + 8); the same for every block.
+  uint32_t lane_off[2];
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok)
+    lane_off[tok] = static_cast<uint32_t>(((grp + 8 * tok) * tok_stride + g * RW +
+                                           S::chunk_word(0, sub)) * 4);
+  const uint32_t* kcache = static_cast<const uint32_t*>(a.k_cache);
+  const uint32_t* vcache = static_cast<const uint32_t*>(a.v_cache);
 
   struct Frag {
     uint32_t k[2][W];
@@ -118,41 +135,42 @@ __global__ __launch_bounds__(256) void paged_partials_kernel(PagedLaunch a) {
   };
   Frag buf[NBUF];
 
-  auto block_valid = [&](int jj, int& blk) __attribute__((always_inline)) {
-    blk = __builtin_amdgcn_readlane(my_id, jj);
-    return blk >= 0 && blk < a.num_blocks;
+  // Tokens of block jj that hold data: 0 past the partition's last block and
+  // for a table entry outside the pool.
+  auto valid_tokens = [&](int jj, int& blk) __attribute__((always_inline)) {
+    blk = __builtin_amdgcn_readlane(my_id, jj & (kWave - 1));
+    const bool ok_blk = jj < nblk && blk >= 0 && blk < a.num_blocks;
+    const int tb = t_begin + jj * kBlockTokens;
+    return ok_blk ? min(kBlockTokens, t_end - tb) : 0;
   };
 
-  // Loads always target a row inside the pool: a table entry outside
-  // [0, num_blocks) is replaced by block 0 and its tokens are masked in
-  // compute_block; the unused tail of a sequence's last block is read (it is
-  // allocated memory) and masked the same way.
+  // One buffer resource per block and tensor, whose record count ends after
+  // the block's last valid token: rows past it read back as zeros, so the
+  // unused tail of a sequence's last block (allocated, contents arbitrary)
+  // and out-of-pool table entries contribute nothing.
   auto load_block = [&](Frag& f, int jj) __attribute__((always_inline)) {
     int blk;
-    const bool ok_blk = block_valid(jj, blk);
-    const size_t b0 = static_cast<size_t>(ok_blk ? blk : 0) * kBlockTokens + grp;
+    const int nvalid = valid_tokens(jj, blk);
+    const size_t base = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens * tok_stride;
+    const int bytes = nvalid * static_cast<int>(tok_stride) * 4;
+    const BufRsrc rk = make_rsrc(kcache + base, bytes);
+    const BufRsrc rv = make_rsrc(vcache + base, bytes);
 #pragma unroll
-    for (int tok = 0; tok < 2; ++tok) {
-      const size_t row = (b0 + 8 * tok) * tok_stride;
+    for (int tok = 0; tok < 2; ++tok)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        load_words<CW>(&f.k[tok][c * CW], kbase + row + S::chunk_word(c, sub));
-        load_words<CW>(&f.v[tok][c * CW], vbase + row + S::chunk_word(c, sub));
+        buffer_load_words<CW>(&f.k[tok][c * CW], rk, lane_off[tok] + c * 8 * CW * 4);
+        buffer_load_words<CW>(&f.v[tok][c * CW], rv, lane_off[tok] + c * 8 * CW * 4);
       }
-    }
   };
 
   auto compute_block = [&](const Frag& f, int jj) __attribute__((always_inline)) {
     int blk;
-    const bool ok_blk = block_valid(jj, blk);
-    const int tb = t_begin + jj * kBlockTokens;
-    const bool full = ok_blk && tb + kBlockTokens <= t_end;  // wave-uniform
-    bool ok[2];
-#pragma unroll
-    for (int tok = 0; tok < 2; ++tok) ok[tok] = full || (ok_blk && tb + grp + 8 * tok < t_end);
+    const int nvalid = valid_tokens(jj, blk);
     float s[2][HPW];
 #pragma unroll
     for (int tok = 0; tok < 2; ++tok) {
+      const bool ok = grp + 8 * tok < nvalid;
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
         float part = 0.f;
@@ -165,21 +183,20 @@ __global__ __launch_bounds__(256) void paged_partials_kernel(PagedLaunch a) {
           }
         }
         const float z = sum_over_8(part) * sl2;
-        s[tok][h] = ok[tok] ? z : -INFINITY;
+        s[tok][h] = ok ? z : -INFINITY;
       }
     }
-    // V rows as raw words; masked rows may hold anything (NaN included):
-    // their weight is 0 and their words are replaced by 0 so 0 * value = 0.
-    uint32_t vw[2][W];
+    // Rows past the valid tokens were read as zeros: weight 0 times value 0.
+    const uint32_t (&vw)[2][W] = f.v;
+    // For bf16 weights: the V elements of the lane's two tokens, paired per
+    // dimension (shared by all heads of the group).
+    uint32_t vlo[PBF16 ? W : 1], vhi[PBF16 ? W : 1];
+    if constexpr (PBF16) {
 #pragma unroll
-    for (int tok = 0; tok < 2; ++tok)
-#pragma unroll
-      for (int w = 0; w < W; ++w) vw[tok][w] = f.v[tok][w];
-    if (!full) {
-#pragma unroll
-      for (int tok = 0; tok < 2; ++tok)
-#pragma unroll
-        for (int w = 0; w < W; ++w) vw[tok][w] = ok[tok] ? vw[tok][w] : 0u;
+      for (int w = 0; w < W; ++w) {
+        vlo[w] = pair_lo(vw[0][w], vw[1][w]);
+        vhi[w] = pair_hi(vw[0][w], vw[1][w]);
+      }
     }
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
@@ -195,30 +212,42 @@ __global__ __launch_bounds__(256) void paged_partials_kernel(PagedLaunch a) {
       }
       const float p0 = exp2_fast(s[0][h] - m[h]);
       const float p1 = exp2_fast(s[1][h] - m[h]);
-      l[h] += p0 + p1;
+      if constexpr (PBF16) {
+        // Weights rounded to bf16 and paired over the lane's two tokens; the
+        // same rounded weights feed the sum, so the output stays an exact
+        // convex combination of V rows.  Products accumulate in fp32.
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        l[h] = dot2_bf16(pp, kBf16OnePair, l[h]);
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        if constexpr (BF16) {
-          acc[h][2 * w] = fmaf(p1, bf16_lo(vw[1][w]), fmaf(p0, bf16_lo(vw[0][w]), acc[h][2 * w]));
-          acc[h][2 * w + 1] = fmaf(p1, bf16_hi(vw[1][w]), fmaf(p0, bf16_hi(vw[0][w]), acc[h][2 * w + 1]));
-        } else {
-          acc[h][w] = fmaf(p1, __uint_as_float(vw[1][w]), fmaf(p0, __uint_as_float(vw[0][w]), acc[h][w]));
+        for (int w = 0; w < W; ++w) {
+          acc[h][2 * w] = dot2_bf16(pp, vlo[w], acc[h][2 * w]);
+          acc[h][2 * w + 1] = dot2_bf16(pp, vhi[w], acc[h][2 * w + 1]);
+        }
+      } else {
+        l[h] += p0 + p1;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          if constexpr (BF16) {
+            acc[h][2 * w] = fmaf(p1, bf16_lo(vw[1][w]), fmaf(p0, bf16_lo(vw[0][w]), acc[h][2 * w]));
+            acc[h][2 * w + 1] = fmaf(p1, bf16_hi(vw[1][w]), fmaf(p0, bf16_hi(vw[0][w]), acc[h][2 * w + 1]));
+          } else {
+            acc[h][w] = fmaf(p1, __uint_as_float(vw[1][w]), fmaf(p0, __uint_as_float(vw[0][w]), acc[h][w]));
+          }
         }
       }
     }
   };
 
+  // Refills are unconditional: a block past the end gets a zero-length
+  // resource, so its loads touch no memory and keep the buffers in place.
 #pragma unroll
-  for (int s0 = 0; s0 < NBUF; ++s0)
-    if (s0 < nblk) load_block(buf[s0], s0);
+  for (int s0 = 0; s0 < NBUF; ++s0) load_block(buf[s0], s0);
   for (int base = 0; base < nblk; base += NBUF) {
 #pragma unroll
     for (int s0 = 0; s0 < NBUF; ++s0) {
       const int jj = base + s0;
-      if (jj < nblk) {
-        compute_block(buf[s0], jj);
-        if (jj + NBUF < nblk) load_block(buf[s0], jj + NBUF);
-      }
+      if (jj < nblk) compute_block(buf[s0], jj);
+      load_block(buf[s0], jj + NBUF);
     }
   }
 
@@ -265,26 +294,42 @@ __global__ __launch_bounds__(256) void paged_partials_kernel(PagedLaunch a) {
   }
 }
 
-template <bool BF16, int D, int HPW>
-hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
-  constexpr int NBUF = (BF16 && HPW <= 4) ? 3 : 2;
+template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = BF16>
+hipError_t launch_variant(const PagedLaunch& a, hipStream_t stream) {
   const int ratio = a.num_q_heads / a.num_kv_heads;
   const long long units = static_cast<long long>(a.batch) * a.num_partitions * a.num_kv_heads *
                           (ratio / HPW);
-  const long long blocks = (units + 3) / 4;
-  hipLaunchKernelGGL((paged_partials_kernel<BF16, D, HPW, NBUF>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(256), 0, stream, a);
+  const long long blocks = (units + WG - 1) / WG;
+  hipLaunchKernelGGL((paged_partials_kernel<BF16, D, HPW, NBUF, WPE, WG, PBF16>),
+                     dim3(static_cast<unsigned>(blocks)), dim3(64 * WG), 0, stream, a);
   return hipGetLastError();
 }
 
+// Tuned on MI355X (bf16, d_head 128): one head per wave keeps 3 waves per
+// SIMD; four heads per wave need ~200 VGPRs (2 waves per SIMD) and do best
+// with two buffers.  Eight-wave workgroups help when a group's rows are read
+// by several wavefronts (one head per wave, or head chunks of one group).
+template <bool BF16, int D, int HPW>
+hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
+  constexpr bool kWide = BF16 || D < 128;  // register budget allows >= 2 waves
+  constexpr int NBUF = (BF16 && HPW == 1) ? 3 : 2;
+  constexpr int WPE = (HPW == 1 && kWide) ? 3 : (kWide ? 2 : 1);
+  const int ratio = a.num_q_heads / a.num_kv_heads;
+  if constexpr (kWide) {
+    if (HPW == 1 || ratio > HPW) return launch_variant<BF16, D, HPW, NBUF, WPE, 8>(a, stream);
+  }
+  return launch_variant<BF16, D, HPW, NBUF, WPE, 4>(a, stream);
+}
+
+// Groups of more than 4 query heads are split over ratio / 4 wavefronts of the
+// same workgroup; they read the same K/V rows, the second time from cache.
 template <bool BF16, int D>
 hipError_t launch_by_ratio(const PagedLaunch& a, hipStream_t stream) {
   const int ratio = a.num_q_heads / a.num_kv_heads;
   switch (ratio) {
     case 1: return launch_typed<BF16, D, 1>(a, stream);
     case 2: return launch_typed<BF16, D, 2>(a, stream);
-    case 4: return launch_typed<BF16, D, 4>(a, stream);
-    default: return launch_typed<BF16, D, 8>(a, stream);  // 8 and multiples of 8
+    default: return launch_typed<BF16, D, 4>(a, stream);  // multiples of 4
   }
 }
 
@@ -301,7 +346,7 @@ hipError_t launch_by_dim(const PagedLaunch& a, hipStream_t stream) {
 
 bool paged_supported(int head_dim, int ratio, bool /*bf16*/) {
   const bool dim_ok = head_dim == 32 || head_dim == 64 || head_dim == 128;
-  const bool ratio_ok = ratio == 1 || ratio == 2 || ratio == 4 || (ratio % 8 == 0 && ratio <= 64);
+  const bool ratio_ok = ratio == 1 || ratio == 2 || (ratio % 4 == 0 && ratio <= 64);
   return dim_ok && ratio_ok;
 }
 

@@ -29,6 +29,23 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// Pack two fp32 values into one bf16x2 word (round to nearest even); a goes
+// to the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Interleave the bf16 halves of two words: (x.lo, y.lo) and (x.hi, y.hi).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int CTRL>
@@ -83,6 +100,33 @@ __device__ __forceinline__ void store_words(uint32_t* dst, const uint32_t* src) 
     v.x = src[0]; v.y = src[1]; v.z = src[2]; v.w = src[3];
   }
   *reinterpret_cast<V*>(dst) = v;
+}
+
+
+// Raw buffer access.  A buffer resource (base, byte count) lives in scalar
+// registers; a load whose byte offset falls at or past the count returns
+// zeros instead of touching memory.  The resource word-3 value selects 32-bit
+// raw addressing on CDNA (gfx9 family).
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           kRsrcWord3);
+}
+
+// Load N consecutive 32-bit words (N = 1, 2 or 4) at byte offset `off`.
+template <int N>
+__device__ __forceinline__ void buffer_load_words(uint32_t* dst, BufRsrc r, uint32_t off) {
+  if constexpr (N == 1) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (N == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    dst[0] = v[0]; dst[1] = v[1];
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+  }
 }
 
 }  // namespace kvd

@@ -41,7 +41,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_llama3_8b",
-                    choices=["gqa_llama3_8b", "mha_llama2_7b", "long_gqa_split", "tiny"])
+                    choices=["gqa_llama3_8b", "mha_llama2_7b", "long_gqa_split", "tiny",
+                             "mla_deepseek_v2"])
+    ap.add_argument("--replicas", type=int, default=4,
+                    help="MLA: rotate over this many copies of the latent cache so the "
+                         "timed reads come from HBM, not the 256 MB Infinity Cache")
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition tokens (-1: the workload's own, 0: library auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -137,6 +141,107 @@ def cpu_baseline(inp, target_s):
             "tokens_per_s": done / dt}
 
 
+def cpu_baseline_mla(inp, target_s, scale):
+    """Time the fp64 oracle on whole sequences of the MLA workload until ~target_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    done = tokens = 0
+    for b in np.random.default_rng(0).permutation(inp.B):
+        sl = slice(int(b), int(b) + 1)
+        oracle.mla_decode_paged(inp.q[sl], inp.c_pool, inp.block_table[sl], inp.seq_lens[sl],
+                                inp.d_c, scale, c_new=inp.c_new[sl])
+        done += 1
+        tokens += int(inp.seq_lens[b])
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens * inp.width * 2 / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {inp.B} sequences ({tokens} positions, all {inp.H} heads) in "
+                      f"{dt:.1f} s; fp64 numpy on {os.cpu_count()} host CPUs",
+            "tokens_per_s": done / dt}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def main_mla(args, kvd, make_config_inputs):
+    import torch
+    dev = torch.device("cuda:0")
+    inp = make_config_inputs(args.workload, sentinel="zero")[0]
+    pt = args.partition if args.partition > 0 else 0
+    q = up(inp.q, dev)
+    caches = [up(inp.c_pool, dev) for _ in range(max(1, args.replicas))]
+    c_new = up(inp.c_new[:, None, :], dev)
+    table, seq = up(inp.block_table, dev), up(inp.seq_lens, dev)
+    H, L = inp.H, inp.max_seq_len
+    pt_used = kvd.decode_attn_partition_tokens(inp.B, H, 1, inp.d_c, L, pt)
+    ws = kvd.alloc_workspace(inp.B, H, 1, inp.d_c, L, pt)
+    out = torch.empty((inp.B, H, inp.d_c), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = caches[i % len(caches)]
+        kvd.kv_append_paged(c[:, :, None, :], None, c_new, None, table, seq)
+        if ev is not None:
+            ev[0].record(stream)
+        kvd.decode_attn_mla_partials(q, c, table, seq, L, ws, partition_tokens=pt)
+        if ev is not None:
+            ev[1].record(stream)
+        kvd.decode_attn_merge(out, seq, 1, L, ws, partition_tokens=pt)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    part_avg = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kv_bytes = inp.kv_bytes_read
+    positions = int(inp.seq_lens.astype(np.int64).sum())
+    flops = positions * H * (inp.width + inp.d_c) * 2
+    achieved = kv_bytes / (part_avg / 1e3) / 1e9
+    tflops = flops / (part_avg / 1e3) / 1e12
+    value = kv_bytes / (ms_step / 1e3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": H, "d_c": inp.d_c,
+                   "d_rope": inp.d_rope, "block_size": 16, "sum_seq_len": positions,
+                   "max_seq_len": L, "partition_tokens": pt_used, "cache_replicas": len(caches)},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(inp.B / (ms_step / 1e3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "flops_per_step": flops,
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {"partials_avg": round(part_avg, 5)},
+        "roofline": {"bound": "hbm", "kernel": "mla_partials_kernel", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("mla_partials", args.workload)},
+        "mfma": {"achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_mla(inp, args.cpu_seconds, kvd.mla_default_scale())
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -154,6 +259,9 @@ def main():
     from workloads import make_config_inputs, config
 
     cfg = config(args.workload)
+    if cfg["kind"] == "mla":
+        main_mla(args, kvd, make_config_inputs)
+        return
     dev = torch.device("cuda:0")
     inp = make_config_inputs(args.workload, sentinel="zero")[0]
     pt = cfg["partition"] if args.partition < 0 else args.partition

@@ -174,6 +174,51 @@ int decode_attn_merge(void* out, const int32_t* seq_lens, int batch, int num_q_h
                       const void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
                       void* stream);
 
+/*
+ * decode_attn_mla -- absorbed multi-head latent attention decode (bf16).
+ *
+ * The cache keeps one row per token: the latent c_t (d_c values) followed by
+ * the decoupled RoPE key k^R_t (d_rope values); the up-projections are folded
+ * into the query and output projections, so each query head arrives as
+ * q~ = [q~_c (d_c) ; q_R (d_rope)] ("KV Cache（键值缓存）", 2.2 路线一, the MLA
+ * equations and the decoupled-RoPE note; section 4, MLA 的工程含义).
+ *   z_t = scale * q~[b][h] . row_t      for t in [0, seq_lens[b])
+ *   out[b][h] = sum_t softmax(z)_t c_t  (latent space, width d_c)
+ * The caller chooses `scale` (the Python binding defaults to 1/sqrt(d_c/4 +
+ * d_rope), the per-head width of the un-absorbed key when d_c = 4 d_h).
+ * Both products run on bf16 MFMA with fp32 accumulation; softmax weights are
+ * rounded to bf16 before the value product, the sum uses the same weights.
+ *
+ *   out      [batch, num_q_heads, d_c] bf16
+ *   q        [batch, num_q_heads, d_c + d_rope] bf16
+ *   c_cache  [num_blocks, 16, d_c + d_rope] bf16; append rows with
+ *            kv_append_paged (num_kv_heads = 1, head_dim = d_c + d_rope,
+ *            v_cache = v_new = NULL)
+ *   d_c = 512, d_rope = 64; num_q_heads a multiple of 16
+ *   partition_tokens 0 (automatic) or a multiple of 32
+ *   workspace >= decode_attn_workspace_bytes(batch, num_q_heads, 1, d_c,
+ *            max_seq_len, partition_tokens), 256-B aligned
+ * Other arguments, errors and preconditions as for decode_attn_paged.
+ */
+int decode_attn_mla(void* out, const void* q, const void* c_cache,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int batch, int num_q_heads, int d_c, int d_rope, int block_size,
+                    int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                    int partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * decode_attn_mla_partials -- first phase of decode_attn_mla only (same
+ * arguments minus `out`); finish with decode_attn_merge(out, seq_lens, batch,
+ * num_q_heads, 1, d_c, max_seq_len, partition_tokens, workspace, ..., KVD_BF16).
+ */
+int decode_attn_mla_partials(const void* q, const void* c_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int batch, int num_q_heads, int d_c, int d_rope, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                             float scale, int partition_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

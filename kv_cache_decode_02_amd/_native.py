@@ -45,6 +45,11 @@ lib.decode_attn_paged.restype = _i
 lib.decode_attn_paged.argtypes = [_vp] + _PAGED_ARGS
 lib.decode_attn_paged_partials.restype = _i
 lib.decode_attn_paged_partials.argtypes = _PAGED_ARGS
+_MLA_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+lib.decode_attn_mla.restype = _i
+lib.decode_attn_mla.argtypes = [_vp] + _MLA_ARGS
+lib.decode_attn_mla_partials.restype = _i
+lib.decode_attn_mla_partials.argtypes = _MLA_ARGS
 lib.decode_attn_merge.restype = _i
 lib.decode_attn_merge.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]
 
@@ -191,3 +196,55 @@ def decode_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, parti
                                    workspace.numel() * workspace.element_size(),
                                    _dtype_code(out), _stream(stream))
     _check(status, "decode_attn_merge")
+
+
+MLA_D_C = 512
+MLA_D_ROPE = 64
+
+
+def mla_default_scale(d_c=MLA_D_C, d_rope=MLA_D_ROPE):
+    """1/sqrt(d_c/4 + d_rope): the un-absorbed per-head key width when d_c = 4 d_h."""
+    return 1.0 / math.sqrt(d_c // 4 + d_rope)
+
+
+def _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale, partition_tokens, ws):
+    for t, n in ((q, "q"), (c_cache, "c_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"), (ws, "workspace")):
+        _need(t, n)
+    _need(q, "q", dtype=torch.bfloat16)
+    _need(c_cache, "c_cache", dtype=torch.bfloat16)
+    _need(block_table, "block_table", dtype=torch.int32)
+    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    B, h, w = q.shape
+    nb, bs = c_cache.shape[0], c_cache.shape[1]
+    if c_cache.shape[-1] != w or c_cache.numel() != nb * bs * w:
+        raise KvdError("c_cache must be [num_blocks, 16, d_c + d_rope] like q's rows")
+    if scale is None:
+        scale = mla_default_scale(d_c, w - d_c)
+    return [_ptr(q), _ptr(c_cache), _ptr(block_table), _ptr(seq_lens), B, h, d_c, w - d_c, bs,
+            block_table.shape[1], nb, int(max_seq_len), float(scale), int(partition_tokens),
+            _ptr(ws), ws.numel() * ws.element_size()]
+
+
+def decode_attn_mla(q, c_cache, block_table, seq_lens, max_seq_len, d_c=MLA_D_C, scale=None,
+                    partition_tokens=0, workspace=None, out=None, stream=None):
+    """Absorbed-MLA decode of q [B, H, d_c + d_rope] over the latent cache; returns
+    out [B, H, d_c] (bf16)."""
+    B, h, _ = q.shape
+    if workspace is None:
+        workspace = alloc_workspace(B, h, 1, d_c, max_seq_len, partition_tokens, device=q.device)
+    if out is None:
+        out = torch.empty((B, h, d_c), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", dtype=torch.bfloat16)
+    args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
+                     partition_tokens, workspace)
+    _check(lib.decode_attn_mla(_ptr(out), *args, _stream(stream)), "decode_attn_mla")
+    return out
+
+
+def decode_attn_mla_partials(q, c_cache, block_table, seq_lens, max_seq_len, workspace,
+                             d_c=MLA_D_C, scale=None, partition_tokens=0, stream=None):
+    """First phase of decode_attn_mla; finish with decode_attn_merge(out, seq_lens, 1, ...)."""
+    args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
+                     partition_tokens, workspace)
+    _check(lib.decode_attn_mla_partials(*args, _stream(stream)), "decode_attn_mla_partials")

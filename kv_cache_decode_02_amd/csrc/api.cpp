@@ -293,4 +293,75 @@ int decode_attn_paged(void* out, const void* q, const void* k_cache, const void*
   return hip_status(launch_merge(m, st));
 }
 
+static int mla_setup(const void* q, const void* c_cache, const int32_t* block_table,
+                     const int32_t* seq_lens, int batch, int num_q_heads, int d_c, int d_rope,
+                     int block_size, int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                     float scale, int partition_tokens, void* workspace, size_t workspace_bytes,
+                     Sizes* s, MlaLaunch* a) {
+  if (batch < 0 || num_q_heads < 1) return KVD_ERR_SHAPE;
+  if (!mla_supported(num_q_heads, d_c, d_rope)) return KVD_ERR_UNSUPPORTED;
+  int rc = check_table(block_size, max_blocks_per_seq, num_blocks, max_seq_len);
+  if (rc) return rc;
+  // Tiles are 32 tokens: an explicit partition must be a multiple of 32.
+  if (partition_tokens > 0 && partition_tokens % 32 != 0) return KVD_ERR_SHAPE;
+  rc = plan(batch, num_q_heads, 1, d_c, max_seq_len, partition_tokens, s);
+  if (rc) return rc;
+  if (batch == 0) return KVD_OK;
+  if (!q || !c_cache || !block_table || !seq_lens) return KVD_ERR_NULL;
+  if (!workspace || workspace_bytes < s->ws.total) return KVD_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(c_cache) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return KVD_ERR_SHAPE;
+  a->q = q;
+  a->c_cache = c_cache;
+  a->block_table = block_table;
+  a->seq_lens = seq_lens;
+  a->ws_o = static_cast<float*>(workspace);
+  a->ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + s->ws.ml_offset);
+  a->batch = batch;
+  a->num_heads = num_q_heads;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->num_blocks = num_blocks;
+  a->max_seq_len = max_seq_len;
+  a->partition_tokens = s->pt;
+  a->num_partitions = s->parts;
+  a->scale = scale;
+  return KVD_OK;
+}
+
+int decode_attn_mla_partials(const void* q, const void* c_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int batch, int num_q_heads, int d_c, int d_rope, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                             float scale, int partition_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Sizes s;
+  MlaLaunch a;
+  const int rc = mla_setup(q, c_cache, block_table, seq_lens, batch, num_q_heads, d_c, d_rope,
+                           block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale,
+                           partition_tokens, workspace, workspace_bytes, &s, &a);
+  if (rc || batch == 0) return rc;
+  return hip_status(launch_mla_partials(a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_mla(void* out, const void* q, const void* c_cache,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int batch, int num_q_heads, int d_c, int d_rope, int block_size,
+                    int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                    int partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  Sizes s;
+  MlaLaunch a;
+  int rc = mla_setup(q, c_cache, block_table, seq_lens, batch, num_q_heads, d_c, d_rope,
+                     block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale,
+                     partition_tokens, workspace, workspace_bytes, &s, &a);
+  if (rc || batch == 0) return rc;
+  if (!out) return KVD_ERR_NULL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(launch_mla_partials(a, st));
+  if (rc) return rc;
+  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, d_c, max_seq_len,
+                                     workspace, KVD_BF16, s);
+  return hip_status(launch_merge(m, st));
+}
+
 }  // extern "C"

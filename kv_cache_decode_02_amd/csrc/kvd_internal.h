@@ -58,12 +58,26 @@ struct AppendLaunch {
   bool vec16;  // all four row buffers 16-byte aligned
 };
 
+struct MlaLaunch {
+  const void* q;            // [B, H, d_c + d_rope] bf16
+  const void* c_cache;      // [NB, 16, d_c + d_rope] bf16
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* ws_o;
+  float* ws_ml;
+  int batch, num_heads, max_blocks_per_seq, num_blocks, max_seq_len;
+  int partition_tokens, num_partitions;
+  float scale;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream);
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
+hipError_t launch_mla_partials(const MlaLaunch& a, hipStream_t stream);
 
 // Whether a kernel instance exists for this head_dim / group ratio / dtype.
 bool paged_supported(int head_dim, int ratio, bool bf16);
+bool mla_supported(int num_heads, int d_c, int d_rope);
 
 }  // namespace kvd

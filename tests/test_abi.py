@@ -113,3 +113,28 @@ def test_merge_rejections():
     assert f(None, P, 2, 32, 8, 128, 1024, 0, P, 1 << 40, 1, None) == ENULL
     assert f(P, P, 2, 32, 8, 96, 1024, 0, P, 1 << 40, 1, None) == EUNSUP
     assert f(P, P, 2, 32, 8, 128, 1024, 0, P, 16, 1, None) == EWS
+
+
+def mla(**kw):
+    a = dict(o=P, q=P, c=P, bt=P, sl=P, B=2, h=128, dc=512, dr=64, bs=16, mb=256, nb=512,
+             L=4096, scale=0.07, pt=0, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.decode_attn_mla(a["o"], a["q"], a["c"], a["bt"], a["sl"], a["B"], a["h"], a["dc"],
+                               a["dr"], a["bs"], a["mb"], a["nb"], a["L"], a["scale"], a["pt"],
+                               a["ws"], a["wsb"], None)
+
+
+def test_mla_rejections():
+    assert mla(q=None) == ENULL
+    assert mla(o=None) == ENULL
+    assert mla(c=None) == ENULL
+    assert mla(dc=256) == EUNSUP
+    assert mla(dr=32) == EUNSUP
+    assert mla(h=24) == EUNSUP            # not a multiple of 16
+    assert mla(pt=48) == ESHAPE           # partitions are whole 32-token tiles
+    assert mla(bs=32) == EUNSUP
+    assert mla(L=256 * 16 + 1) == ESHAPE
+    assert mla(ws=None) == EWS
+    need = kvd.decode_attn_workspace_bytes(2, 128, 1, 512, 4096, 0)
+    assert mla(wsb=need - 1) == EWS
+    assert mla(B=0, q=None, o=None, ws=None, wsb=0) == OK

@@ -47,6 +47,7 @@ constexpr int kLoadsPerThread = kBlockTokens * kChunks / (kThreads / 2);  // 9
 constexpr int kHeadsPerWave = 16;
 constexpr int kHeadsPerGroup = 4 * kHeadsPerWave;
 constexpr int kKSteps = kW / 32;          // 18
+constexpr int kKBatch = 3;                // K-steps whose LDS reads are in flight together
 constexpr int kNTiles = kDc / 16;         // 32
 constexpr float kRaise = 8.0f;
 
@@ -79,7 +80,7 @@ struct MlaLaunchDev {
 };
 
 __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kTile * kLdsRow];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -124,11 +125,12 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
 
   // Tile loads: waves 0-1 fetch the tile's first 16-token block, waves 2-3
   // the second, 9 chunks of 16 B per thread (a block is 16 x 1152 contiguous
-  // bytes), so every load instruction uses one wave-uniform buffer resource.
+  // bytes), so every load instruction uses one wave-uniform buffer resource
+  // whose byte count ends at the block's last valid row.
   const int half = wave_uniform(wave >> 1);
   const int lt = tid & 127;
-  uint32_t pre[kLoadsPerThread][4];
-  auto load_tile = [&](int ti) __attribute__((always_inline)) {
+  uint32_t pre[2][kLoadsPerThread][4];
+  auto load_tile = [&](int ti, uint32_t (&dst)[kLoadsPerThread][4]) __attribute__((always_inline)) {
     const int t0 = t_begin + ti * kTile + half * kBlockTokens;
     int blk = -1;
     if (ti < ntiles && t0 < t_end) blk = trow[t0 / kBlockTokens];
@@ -138,22 +140,18 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
                                 nvalid * kRowBytes);
 #pragma unroll
     for (int c = 0; c < kLoadsPerThread; ++c)
-      buffer_load_words<4>(pre[c], r, static_cast<uint32_t>((lt + 128 * c) * 16));
+      buffer_load_words<4>(dst[c], r, static_cast<uint32_t>((lt + 128 * c) * 16));
   };
-  auto store_tile = [&]() __attribute__((always_inline)) {
+  auto store_tile = [&](const uint32_t (&src)[kLoadsPerThread][4], uint8_t* tile)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < kLoadsPerThread; ++c) {
       const int qi = lt + 128 * c;
       const int row = half * kBlockTokens + qi / kChunks, ch = qi % kChunks;
       *reinterpret_cast<uint4*>(tile + row * kLdsRow + ch * 16) =
-          make_uint4(pre[c][0], pre[c][1], pre[c][2], pre[c][3]);
+          make_uint4(src[c][0], src[c][1], src[c][2], src[c][3]);
     }
   };
-
-  load_tile(0);
-  store_tile();
-  __syncthreads();
-  if (ntiles > 1) load_tile(1);
 
   // Valid rows of each 16-token half of tile ti (0 for a table entry outside
   // the pool, whose rows were read as zeros and must not get weight).
@@ -164,84 +162,117 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
     return (blk >= 0 && blk < a.num_blocks) ? min(kBlockTokens, t_end - t0) : 0;
   };
 
-  for (int ti = 0; ti < ntiles; ++ti) {
+  auto compute_tile = [&](int ti, const uint8_t* tile) __attribute__((always_inline)) {
+    if (!active) return;
     const int nv0 = half_valid(ti, 0), nv1 = half_valid(ti, 1);
-    if (active) {
-      // Scores S^T: lane gets head head0 + col, tokens 16 mt + 4 kb + i.
-      f32x4_t s[2];
+    // Scores S^T: lane gets head head0 + col, tokens 16 mt + 4 kb + i.  Two
+    // independent accumulator chains per token half keep the MFMA pipe fed.
+    f32x4_t s[2][2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint8_t* arow = tile + (16 * mt + col) * kLdsRow + 16 * kb;
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // LDS reads are issued in batches of kKBatch K-steps ahead of their
+    // MFMAs so that their latency overlaps.
+    const uint8_t* arow = tile + col * kLdsRow + 16 * kb;
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          const uint4 av = *reinterpret_cast<const uint4*>(arow + 64 * ks);
-          s[mt] = mfma16(as_bf16x8(av.x, av.y, av.z, av.w),
-                         as_bf16x8(qf[ks][0], qf[ks][1], qf[ks][2], qf[ks][3]), s[mt]);
-        }
-      }
-      float z[2][4];
-      float mx = -INFINITY;
+    for (int ks0 = 0; ks0 < kKSteps; ks0 += kKBatch) {
+      uint4 av[kKBatch][2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int k = 0; k < kKBatch; ++k)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = 4 * kb + i < (mt ? nv1 : nv0);
-          z[mt][i] = ok ? s[mt][i] * sl2 : -INFINITY;
-          mx = fmaxf(mx, z[mt][i]);
-        }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const bool up = mx > m_run + kRaise;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float mn = up ? mx : m_run;
-        const float alpha = exp2_fast(m_run - mn);  // per head (col)
-        l_lane *= alpha;
-        // O rows are heads 4 kb + i: fetch those heads' factors.
-        float al[4];
+        for (int mt = 0; mt < 2; ++mt)
+          av[k][mt] = *reinterpret_cast<const uint4*>(arow + 16 * mt * kLdsRow + 64 * (ks0 + k));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i, kWave);
+      for (int k = 0; k < kKBatch; ++k) {
+        const int ks = ks0 + k;
+        const bf16x8_t bq = as_bf16x8(qf[ks][0], qf[ks][1], qf[ks][2], qf[ks][3]);
 #pragma unroll
-        for (int nt = 0; nt < kNTiles; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[nt][i] *= al[i];
-        m_run = mn;
-      }
-      // Weights as the A operand: K-slot j < 4 is token 4 kb + j, j >= 4 is
-      // token 16 + 4 kb + (j - 4).
-      uint32_t pw[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const float p0 = exp2_fast(z[mt][0] - m_run), p1 = exp2_fast(z[mt][1] - m_run);
-        const float p2 = exp2_fast(z[mt][2] - m_run), p3 = exp2_fast(z[mt][3] - m_run);
-        pw[2 * mt] = pack_bf16x2(p0, p1);
-        pw[2 * mt + 1] = pack_bf16x2(p2, p3);
-        l_lane = dot2_bf16(pw[2 * mt], kBf16OnePair, l_lane);
-        l_lane = dot2_bf16(pw[2 * mt + 1], kBf16OnePair, l_lane);
-      }
-      const bf16x8_t pa = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
-      // Values: lane (col, kb) of the transpose load supplies row
-      // T + col / 4 and latent columns 16 nt + 4 (col % 4) .. + 3.
-      const uint8_t* vrow0 = tile + (4 * kb + (col >> 2)) * kLdsRow + 8 * (col & 3);
-      const uint8_t* vrow1 = vrow0 + 16 * kLdsRow;
-#pragma unroll
-      for (int nt = 0; nt < kNTiles; ++nt) {
-        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vrow0 + 32 * nt));
-        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vrow1 + 32 * nt));
-        // Whole-vector casts: K-slots 0-3 from v0, 4-7 from v1.
-        const uint2 w0 = __builtin_bit_cast(uint2, v0);
-        const uint2 w1 = __builtin_bit_cast(uint2, v1);
-        acc[nt] = mfma16(pa, as_bf16x8(w0.x, w0.y, w1.x, w1.y), acc[nt]);
+        for (int mt = 0; mt < 2; ++mt)
+          s[mt][ks & 1] = mfma16(as_bf16x8(av[k][mt].x, av[k][mt].y, av[k][mt].z, av[k][mt].w),
+                                 bq, s[mt][ks & 1]);
       }
     }
-    __syncthreads();  // everyone is done with this tile
-    if (ti + 1 < ntiles) {
-      store_tile();
-      __syncthreads();
-      if (ti + 2 < ntiles) load_tile(ti + 2);
+    float z[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = 4 * kb + i < (mt ? nv1 : nv0);
+        z[mt][i] = ok ? (s[mt][0][i] + s[mt][1][i]) * sl2 : -INFINITY;
+        mx = fmaxf(mx, z[mt][i]);
+      }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const bool up = mx > m_run + kRaise;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float mn = up ? mx : m_run;
+      const float alpha = exp2_fast(m_run - mn);  // per head (col)
+      l_lane *= alpha;
+      // O rows are heads 4 kb + i: fetch those heads' factors.
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kb + i, kWave);
+#pragma unroll
+      for (int nt = 0; nt < kNTiles; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nt][i] *= al[i];
+      m_run = mn;
     }
+    // Weights as the A operand: K-slot j < 4 is token 4 kb + j, j >= 4 is
+    // token 16 + 4 kb + (j - 4).
+    uint32_t pw[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const float p0 = exp2_fast(z[mt][0] - m_run), p1 = exp2_fast(z[mt][1] - m_run);
+      const float p2 = exp2_fast(z[mt][2] - m_run), p3 = exp2_fast(z[mt][3] - m_run);
+      pw[2 * mt] = pack_bf16x2(p0, p1);
+      pw[2 * mt + 1] = pack_bf16x2(p2, p3);
+      l_lane = dot2_bf16(pw[2 * mt], kBf16OnePair, l_lane);
+      l_lane = dot2_bf16(pw[2 * mt + 1], kBf16OnePair, l_lane);
+    }
+    const bf16x8_t pa = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+    // Values: lane (col, kb) of the transpose load supplies row
+    // T + col / 4 and latent columns 16 nt + 4 (col % 4) .. + 3.
+    const uint8_t* vrow0 = tile + (4 * kb + (col >> 2)) * kLdsRow + 8 * (col & 3);
+    const uint8_t* vrow1 = vrow0 + 16 * kLdsRow;
+#pragma unroll
+    for (int nt = 0; nt < kNTiles; ++nt) {
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(vrow0 + 32 * nt));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(vrow1 + 32 * nt));
+      // Whole-vector casts: K-slots 0-3 from v0, 4-7 from v1.
+      const uint2 w0 = __builtin_bit_cast(uint2, v0);
+      const uint2 w1 = __builtin_bit_cast(uint2, v1);
+      acc[nt] = mfma16(pa, as_bf16x8(w0.x, w0.y, w1.x, w1.y), acc[nt]);
+    }
+  };
+
+  // Pipeline: tile ti is computed from LDS buffer ti % 2 while tile ti + 1
+  // sits in the other buffer and tiles ti + 2 and ti + 3 are in flight in the
+  // two register slots (slot ti % 2 holds tile ti + 1 at the start of step
+  // ti).  Only the store/refill alternates between the slots, so the compute
+  // body exists once.  One barrier per tile; loads past the last tile get a
+  // zero-length resource (no memory traffic).
+  load_tile(0, pre[0]);
+  store_tile(pre[0], tiles[0]);
+  load_tile(1, pre[0]);
+  load_tile(2, pre[1]);
+  __syncthreads();
+  for (int ti = 0; ti < ntiles; ++ti) {
+    uint8_t* next = tiles[(ti + 1) & 1];
+    if ((ti & 1) == 0) {
+      store_tile(pre[0], next);
+      load_tile(ti + 3, pre[0]);
+    } else {
+      store_tile(pre[1], next);
+      load_tile(ti + 3, pre[1]);
+    }
+    compute_tile(ti, tiles[ti & 1]);
+    __syncthreads();
   }
 
   if (!active) return;

@@ -15,6 +15,8 @@ constexpr int kBlockSize = 16;
 constexpr int kMinPartition = 64;
 constexpr int kMaxPartition = 1024;   // 64 blocks: one block id per lane
 constexpr long long kTargetWaves = 12288;
+constexpr long long kMlaTargetGroups = 256;  // one workgroup per compute unit
+constexpr int kLatentWidth = 512;
 constexpr int kMaxTableBlocks = 1 << 26;  // keeps max_blocks_per_seq * 16 in int
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -32,8 +34,10 @@ int check_heads(int batch, int num_q_heads, int num_kv_heads) {
 }
 
 // Partition size: the given one, or the largest of 1024 .. 64 that still
-// gives at least kTargetWaves wavefronts for a batch at max_seq_len.
-int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int max_seq_len,
+// fills the chip for a batch at max_seq_len: kTargetWaves wavefronts for the
+// paged kernel, one 512-thread workgroup per compute unit for the latent
+// (MLA) kernel, whose rows are the only ones of width 512.
+int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq_len,
                       int partition_tokens) {
   if (partition_tokens > 0) {
     if (partition_tokens % kBlockSize != 0 || partition_tokens > kMaxPartition) return KVD_ERR_SHAPE;
@@ -41,11 +45,15 @@ int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int max_seq_
   }
   if (partition_tokens < 0) return KVD_ERR_SHAPE;
   const int ratio = num_q_heads / num_kv_heads;
-  const long long units = static_cast<long long>(batch) * num_kv_heads * (ratio / heads_per_wave(ratio));
+  const bool latent = head_dim == kLatentWidth;
+  const long long units =
+      latent ? static_cast<long long>(batch) * mla_head_groups(num_q_heads)
+             : static_cast<long long>(batch) * num_kv_heads * (ratio / heads_per_wave(ratio));
+  const long long target = latent ? kMlaTargetGroups : kTargetWaves;
   int pt = kMaxPartition;
   while (pt > kMinPartition) {
     const long long parts = (max_seq_len + pt - 1) / pt;
-    if (units * parts >= kTargetWaves) break;
+    if (units * parts >= target) break;
     pt /= 2;
   }
   return pt;
@@ -62,7 +70,8 @@ int plan(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq
   int rc = check_heads(batch, num_q_heads, num_kv_heads);
   if (rc) return rc;
   if (head_dim < 1 || max_seq_len < 1) return KVD_ERR_SHAPE;
-  const int pt = resolve_partition(batch, num_q_heads, num_kv_heads, max_seq_len, partition_tokens);
+  const int pt = resolve_partition(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                   partition_tokens);
   if (pt < 0) return pt;
   s->pt = pt;
   s->parts = (max_seq_len + pt - 1) / pt;

@@ -79,5 +79,7 @@ hipError_t launch_mla_partials(const MlaLaunch& a, hipStream_t stream);
 // Whether a kernel instance exists for this head_dim / group ratio / dtype.
 bool paged_supported(int head_dim, int ratio, bool bf16);
 bool mla_supported(int num_heads, int d_c, int d_rope);
+// Workgroups per (sequence, partition): one per 64 query heads.
+int mla_head_groups(int num_heads);
 
 }  // namespace kvd

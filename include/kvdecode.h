@@ -98,7 +98,10 @@ int kv_append_paged(void* k_cache, void* v_cache, const void* k_new, const void*
  * decode_attn_partition_tokens -- the KV partition size (tokens) that the
  * decode calls will use for these sizes: `partition_tokens` itself when it is
  * positive (it must then be a multiple of 16), otherwise the library's
- * automatic choice.  Returns a negative status for invalid sizes.
+ * automatic choice.  For the paged path the automatic choice is 0, the
+ * balanced split (below); for the latent path (head_dim = d_c = 512) and for
+ * batches above 16383 it is a partition size.  Returns a negative status for
+ * invalid sizes.
  */
 int decode_attn_partition_tokens(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_seq_len, int partition_tokens);
@@ -124,11 +127,14 @@ size_t decode_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
  * positions are visible: a single decode row has nothing in its future
  * ("单请求 KV Cache", 改动三).
  *
- * Implementation: positions are cut into partitions of
- * decode_attn_partition_tokens(...) tokens; a first kernel writes each
- * partition's running max, sum and unnormalised output into `workspace`, a
- * second merges the partitions by log-sum-exp into `out`.  The two phases are
- * also exported separately below.
+ * Implementation: positions are cut into pieces; a first kernel writes each
+ * piece's running max, sum and unnormalised output into `workspace`, a
+ * second merges the pieces by log-sum-exp into `out`.  The two phases are
+ * also exported separately below.  With partition_tokens > 0 the pieces are
+ * fixed partitions of that many tokens.  With partition_tokens = 0 (the
+ * balanced split) every compute unit takes an equal share of all blocks of
+ * the batch, whatever the mix of lengths, and a sequence is cut wherever the
+ * shares end (at most ceil(ceil(max_seq_len / 16) / 16) + 1 pieces).
  *
  *   out              [batch, num_q_heads, head_dim], dtype
  *   q                [batch, num_q_heads, head_dim], dtype

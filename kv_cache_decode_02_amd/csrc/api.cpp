@@ -17,6 +17,7 @@ constexpr int kMaxPartition = 1024;   // 64 blocks: one block id per lane
 constexpr long long kTargetWaves = 12288;
 constexpr long long kMlaTargetGroups = 256;  // one workgroup per compute unit
 constexpr int kLatentWidth = 512;
+constexpr int kMaxBalancedBatch = 16383;  // block prefix of the batch in LDS (64 KiB)
 constexpr int kMaxTableBlocks = 1 << 26;  // keeps max_blocks_per_seq * 16 in int
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -60,8 +61,9 @@ int resolve_partition(int batch, int num_q_heads, int num_kv_heads, int head_dim
 }
 
 struct Sizes {
-  int pt;
-  int parts;
+  int pt;         // 0: balanced split
+  int parts;      // partitions, or the bound on pieces per sequence
+  bool balanced;
   WorkspaceLayout ws;
 };
 
@@ -70,18 +72,29 @@ int plan(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_seq
   int rc = check_heads(batch, num_q_heads, num_kv_heads);
   if (rc) return rc;
   if (head_dim < 1 || max_seq_len < 1) return KVD_ERR_SHAPE;
-  const int pt = resolve_partition(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                   partition_tokens);
-  if (pt < 0) return pt;
-  s->pt = pt;
-  s->parts = (max_seq_len + pt - 1) / pt;
+  // Automatic choice for the paged path: the balanced split, unless the
+  // batch is too large for its per-workgroup block prefix or its item count
+  // would leave int range.
+  const long long max_blocks = (max_seq_len + kBlockSize - 1) / kBlockSize;
+  s->balanced = partition_tokens == 0 && head_dim != kLatentWidth && batch <= kMaxBalancedBatch &&
+                static_cast<long long>(batch) * num_q_heads * max_blocks < INT_MAX;
+  if (s->balanced) {
+    s->pt = 0;
+    s->parts = static_cast<int>((max_blocks + kBalancedMinPieceBlocks - 1) / kBalancedMinPieceBlocks) + 1;
+  } else {
+    const int pt = resolve_partition(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                     partition_tokens);
+    if (pt < 0) return pt;
+    s->pt = pt;
+    s->parts = (max_seq_len + pt - 1) / pt;
+  }
   // The grid and the workspace must stay addressable.
   const long long ratio = num_q_heads / num_kv_heads;
   const long long waves = static_cast<long long>(batch) * s->parts * num_kv_heads *
                           (ratio / heads_per_wave(static_cast<int>(ratio)));
   if (waves >= INT_MAX || static_cast<long long>(batch) * num_q_heads >= INT_MAX / 4)
     return KVD_ERR_SHAPE;
-  s->ws = workspace_layout(batch, num_q_heads, s->parts, head_dim);
+  s->ws = workspace_layout(batch, num_q_heads, s->parts, head_dim, s->balanced);
   return KVD_OK;
 }
 
@@ -99,12 +112,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
-WorkspaceLayout workspace_layout(int batch, int num_q_heads, int num_partitions, int head_dim) {
+WorkspaceLayout workspace_layout(int batch, int num_q_heads, int num_partitions, int head_dim,
+                                 bool balanced) {
   WorkspaceLayout w;
   const size_t slots = static_cast<size_t>(batch) * num_q_heads * num_partitions;
   w.o_bytes = slots * head_dim * sizeof(float);
   w.ml_offset = align256(w.o_bytes);
-  w.total = w.ml_offset + align256(slots * 2 * sizeof(float));
+  w.counts_offset = w.ml_offset + align256(slots * 2 * sizeof(float));
+  const size_t counts = balanced ? static_cast<size_t>(batch) * num_q_heads * sizeof(int32_t) : 0;
+  w.total = w.counts_offset + align256(counts);
   return w;
 }
 
@@ -220,6 +236,9 @@ static PagedLaunch paged_launch(const void* q, const void* k_cache, const void* 
   a.num_partitions = s.parts;
   a.scale = scale;
   a.bf16 = dtype == KVD_BF16;
+  a.counts = s.balanced
+                 ? reinterpret_cast<int*>(static_cast<char*>(workspace) + s.ws.counts_offset)
+                 : nullptr;
   return a;
 }
 
@@ -238,6 +257,9 @@ static MergeLaunch merge_launch(void* out, const int32_t* seq_lens, int batch, i
   m.partition_tokens = s.pt;
   m.num_partitions = s.parts;
   m.bf16 = dtype == KVD_BF16;
+  m.counts = s.balanced ? reinterpret_cast<const int*>(static_cast<const char*>(workspace) +
+                                                       s.ws.counts_offset)
+                        : nullptr;
   return m;
 }
 

@@ -6,7 +6,9 @@
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,
 // the exact regrouping of the stable softmax of "KV缓存原理与显存估算"
 // (知识点二: subtracting one common maximum leaves the softmax unchanged).
-// A sequence with no positions gets zeros.
+// A sequence with no positions gets zeros.  Fixed partitions: P_b =
+// ceil(L_b / partition); balanced split: P_b is the piece count that the
+// partial kernel recorded.
 #include "kvd_device.h"
 #include "kvd_internal.h"
 
@@ -23,31 +25,60 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
 
   int len = a.seq_lens[b];
   len = min(len, a.max_blocks_per_seq_tokens);
-  const int np = len > 0 ? (len + a.partition_tokens - 1) / a.partition_tokens : 0;
   const size_t P = a.num_partitions;
+  int np = len <= 0 ? 0 : a.counts ? a.counts[bh] : (len + a.partition_tokens - 1) / a.partition_tokens;
+  np = min(max(np, 0), static_cast<int>(P));
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + bh * P;
   const float* o = a.ws_o + bh * P * D;
 
+  // Pass 1, lanes over slots: the common maximum.  Slots with l = 0 (empty
+  // markers of the streamed split, or pieces without valid tokens) carry no
+  // weight and are skipped.
   float M = kMinusBig;
-  for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[p].x);
+  for (int p = lane; p < np; p += kWave) {
+    const float2 v = ml[p];
+    if (v.y > 0.f) M = fmaxf(M, v.x);
+  }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
 
+  // Pass 2: 64 slots at a time, the non-empty ones from a ballot; their
+  // weights come from the owning lane, their rows are read 4 at a time.
   const bool active = lane * DL < D;
   float acc[DL];
 #pragma unroll
   for (int d = 0; d < DL; ++d) acc[d] = 0.f;
   float den = 0.f;
-#pragma unroll 4
-  for (int p = 0; p < np; ++p) {
-    const float2 v = ml[p];
-    const float w = exp2_fast(v.x - M);
-    den = fmaf(w, v.y, den);
-    if (active) {
+  for (int p0 = 0; p0 < np; p0 += kWave) {
+    const float2 v = p0 + lane < np ? ml[p0 + lane] : make_float2(kMinusBig, 0.f);
+    const float w_lane = v.y > 0.f ? exp2_fast(v.x - M) : 0.f;
+    den += w_lane * v.y;
+    uint64_t mask = __builtin_amdgcn_ballot_w64(v.y > 0.f);
+    while (mask) {
+      int idx[4];
 #pragma unroll
-      for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, o[p * D + lane * DL + d], acc[d]);
+      for (int k = 0; k < 4; ++k) {
+        idx[k] = mask ? static_cast<int>(__builtin_ctzll(mask)) : -1;
+        mask &= mask - 1;
+      }
+      float rows[4][DL];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int d = 0; d < DL; ++d)
+          rows[k][d] = (idx[k] >= 0 && active) ? o[(p0 + idx[k]) * D + lane * DL + d] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float w = __shfl(w_lane, idx[k] >= 0 ? idx[k] : 0, kWave);
+        if (idx[k] >= 0) {
+#pragma unroll
+          for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);
+        }
+      }
     }
   }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) den += shfl_xor_f(den, s);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   if (active) {
     if constexpr (BF16) {

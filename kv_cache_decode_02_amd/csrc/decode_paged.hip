@@ -1,32 +1,35 @@
-// Split-KV decode attention over a paged cache: per-partition partials.
+// Split-KV decode attention over a paged cache: partial results.
 //
 // What is computed (per sequence b, query head h, K/V head g = h / r):
 //   z_t = scale * q . K_t,  out = sum_t softmax(z)_t V_t  over t < seq_lens[b]
 // ("KV缓存原理与显存估算", 知识点二, the z / a / o equations; the single
 // decode row sees every cached position, "单请求 KV Cache", 改动三).
-// The positions are cut into partitions; this kernel produces, for each
-// (b, h, partition), the running maximum m (log2 units), the sum
-// l = sum 2^(z' - m) and the unnormalised acc = sum 2^(z' - m) V_t, with
-// z' = z * log2(e).  decode_merge.hip combines the partitions.
+// The positions are cut into pieces; for each (b, h, piece) a kernel here
+// writes the running maximum m (log2 units), the sum l = sum 2^(z' - m) and
+// the unnormalised acc = sum 2^(z' - m) V_t, with z' = z * log2(e).
+// decode_merge.hip combines the pieces.
 //
-// Work decomposition (one wavefront = one unit):
-//   unit = (b, partition, kv head g, chunk of HPW query heads of the group)
-//   The 64 lanes form 8 groups of 8 lanes.  For each 16-token block the
-//   group k handles tokens k and k + 8; inside a group each lane owns D/8
-//   dimensions of the row, loaded as 16-byte (or 8-byte) vectors laid out so
-//   that one load instruction of the 8 lanes covers a contiguous 128 B of the
-//   row.  A K/V row is loaded from HBM once and used by all HPW query heads
-//   from registers (the GQA sharing), so the cache is read exactly once.
+// Per wavefront: a unit is one KV head g and a chunk of HPW query heads of
+// its group.  The 64 lanes form 8 groups of 8 lanes.  For each 16-token block
+// the group k handles tokens k and k + 8; inside a group each lane owns D/8
+// dimensions of the row, loaded as 16-byte (or 8-byte) vectors laid out so
+// that one load instruction of the 8 lanes covers a contiguous 128 B of the
+// row.  A K/V row is loaded from HBM once and used by all HPW query heads from
+// registers (the GQA sharing), so the cache is read exactly once.
 //   Scores: per-lane bf16 dot2 partial sums, reduced over the 8 lanes of the
 //   group with DPP moves.
-//   Softmax: every lane group keeps its own running max; the reference max
-//   is only raised when a score exceeds it by more than kRaise (log2 units),
+//   Softmax: every lane group keeps its own running max; the reference max is
+//   only raised when a score exceeds it by more than kRaise (log2 units),
 //   which keeps every exponential below 2^kRaise and makes rescaling of the
-//   accumulators rare.  The groups are merged once at the end with shuffles.
-//   Latency: the 16-token blocks of a partition are streamed through NBUF
-//   register buffers, so NBUF - 1 blocks of loads are in flight while one is
-//   being computed; the partition's block ids are read once, one per lane,
-//   and broadcast with readlane.
+//   accumulators rare.  The groups are merged when a piece is written.
+//   Latency: blocks stream through NBUF register buffers, so NBUF - 1 blocks
+//   of loads are in flight while one is being computed.
+//
+// Two decompositions:
+//   fixed partitions (partition_tokens > 0): one wavefront per (b, partition,
+//     unit), paged_partials_kernel;
+//   balanced split (automatic mode): one workgroup per compute unit, each
+//     streaming an equal share of all blocks, paged_balanced_kernel.
 #include "kvd_device.h"
 #include "kvd_internal.h"
 
@@ -35,6 +38,7 @@ namespace {
 
 constexpr float kRaise = 8.0f;
 constexpr int kMaxPartitionBlocks = 64;  // one block id per lane
+constexpr int kMinPieceBlocks = kBalancedMinPieceBlocks;
 
 template <bool BF16, int D>
 struct RowShape {
@@ -54,24 +58,313 @@ struct RowShape {
   }
 };
 
+// Running softmax state of HPW query heads; each lane holds its D / 8
+// dimensions of every accumulator.
+template <int HPW, int DPL>
+struct HeadState {
+  float m[HPW], l[HPW], acc[HPW][DPL];
+};
+
+template <int HPW, int DPL>
+__device__ __forceinline__ void reset_state(HeadState<HPW, DPL>& st) {
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    st.m[h] = kMinusBig;
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) st.acc[h][e] = 0.f;
+  }
+}
+
+// The K and V rows of the lane's two token slots of one block.
+template <bool BF16, int D>
+struct Frag {
+  uint32_t k[2][RowShape<BF16, D>::W];
+  uint32_t v[2][RowShape<BF16, D>::W];
+};
+
+// Query slice of heads h0 .. h0 + HPW - 1 of sequence b, in the lane layout of
+// the K rows.
+template <bool BF16, int D, int HPW>
+__device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b, int h0,
+                                           uint32_t (&qv)[HPW][RowShape<BF16, D>::W]) {
+  using S = RowShape<BF16, D>;
+  const int sub = lane & 7;
+  const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
+                       (static_cast<size_t>(b) * a.num_q_heads + h0) * S::RW;
+#pragma unroll
+  for (int h = 0; h < HPW; ++h)
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c)
+      load_words<S::CW>(&qv[h][c * S::CW], qw + h * S::RW + S::chunk_word(c, sub));
+}
+
+// Issues the loads of physical block `blk` for KV head g: the lane's two token
+// rows of K and V.  One buffer resource per tensor whose record count ends
+// after the block's nvalid valid tokens: rows past them (the unused tail of a
+// sequence's last block, contents arbitrary) and a block with nvalid == 0
+// read back as zeros without touching memory.
+template <bool BF16, int D>
+__device__ __forceinline__ void load_block(Frag<BF16, D>& f, const PagedLaunch& a, int lane, int g,
+                                           int blk, int nvalid) {
+  using S = RowShape<BF16, D>;
+  const int grp = lane >> 3;
+  const int sub = lane & 7;
+  const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * S::RW;  // words per token
+  const size_t base = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens * tok_stride;
+  const int bytes = nvalid * static_cast<int>(tok_stride) * 4;
+  const BufRsrc rk = make_rsrc(static_cast<const uint32_t*>(a.k_cache) + base, bytes);
+  const BufRsrc rv = make_rsrc(static_cast<const uint32_t*>(a.v_cache) + base, bytes);
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    const uint32_t off = static_cast<uint32_t>(
+        ((grp + 8 * tok) * tok_stride + g * S::RW + S::chunk_word(0, sub)) * 4);
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c) {
+      buffer_load_words<S::CW>(&f.k[tok][c * S::CW], rk, off + c * 8 * S::CW * 4);
+      buffer_load_words<S::CW>(&f.v[tok][c * S::CW], rv, off + c * 8 * S::CW * 4);
+    }
+  }
+}
+
+// One block through the online softmax of HPW heads; nvalid tokens count.
+template <bool BF16, int D, int HPW, bool PBF16>
+__device__ __forceinline__ void softmax_block(const Frag<BF16, D>& f,
+                                              const uint32_t (&qv)[HPW][RowShape<BF16, D>::W],
+                                              int lane, int nvalid, float sl2,
+                                              HeadState<HPW, D / 8>& st) {
+  static_assert(BF16 || !PBF16, "bf16 weights need a bf16 cache");
+  using S = RowShape<BF16, D>;
+  constexpr int W = S::W, DPL = S::DPL;
+  const int grp = lane >> 3;
+  float (&m)[HPW] = st.m;
+  float (&l)[HPW] = st.l;
+  float (&acc)[HPW][DPL] = st.acc;
+  float s[2][HPW];
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    const bool ok = grp + 8 * tok < nvalid;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      float part = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        if constexpr (BF16) {
+          part = dot2_bf16(qv[h][w], f.k[tok][w], part);
+        } else {
+          part = fmaf(__uint_as_float(qv[h][w]), __uint_as_float(f.k[tok][w]), part);
+        }
+      }
+      const float z = sum_over_8(part) * sl2;
+      s[tok][h] = ok ? z : -INFINITY;
+    }
+  }
+  // Rows past the valid tokens were read as zeros: weight 0 times value 0.
+  const uint32_t (&vw)[2][W] = f.v;
+  // For bf16 weights: the V elements of the lane's two tokens, paired per
+  // dimension (shared by all heads of the group).
+  uint32_t vlo[PBF16 ? W : 1], vhi[PBF16 ? W : 1];
+  if constexpr (PBF16) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      vlo[w] = pair_lo(vw[0][w], vw[1][w]);
+      vhi[w] = pair_hi(vw[0][w], vw[1][w]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    const float mx = fmaxf(s[0][h], s[1][h]);
+    const bool up = mx > m[h] + kRaise;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float mn = up ? mx : m[h];
+      const float alpha = exp2_fast(m[h] - mn);
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
+      m[h] = mn;
+    }
+    const float p0 = exp2_fast(s[0][h] - m[h]);
+    const float p1 = exp2_fast(s[1][h] - m[h]);
+    if constexpr (PBF16) {
+      // Weights rounded to bf16 and paired over the lane's two tokens; the
+      // same rounded weights feed the sum, so the output stays an exact
+      // convex combination of V rows.  Products accumulate in fp32.
+      const uint32_t pp = pack_bf16x2(p0, p1);
+      l[h] = dot2_bf16(pp, kBf16OnePair, l[h]);
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        acc[h][2 * w] = dot2_bf16(pp, vlo[w], acc[h][2 * w]);
+        acc[h][2 * w + 1] = dot2_bf16(pp, vhi[w], acc[h][2 * w + 1]);
+      }
+    } else {
+      l[h] += p0 + p1;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        if constexpr (BF16) {
+          acc[h][2 * w] = fmaf(p1, bf16_lo(vw[1][w]), fmaf(p0, bf16_lo(vw[0][w]), acc[h][2 * w]));
+          acc[h][2 * w + 1] =
+              fmaf(p1, bf16_hi(vw[1][w]), fmaf(p0, bf16_hi(vw[0][w]), acc[h][2 * w + 1]));
+        } else {
+          acc[h][w] = fmaf(p1, __uint_as_float(vw[1][w]), fmaf(p0, __uint_as_float(vw[0][w]), acc[h][w]));
+        }
+      }
+    }
+  }
+}
+
+// Combination of x over the 8 lane groups (lanes differing in bits 3..5),
+// on the VALU: a row rotation by 8 pairs lanes l and l ^ 8 inside each
+// 16-lane row, the permlane swaps pair rows (l ^ 16) and halves (l ^ 32).
+// Every lane ends with the same value, since each step combines a lane's
+// value with its partner's in an order-independent way.
+__device__ __forceinline__ float groups_max(float x) {
+  x = fmaxf(x, dpp_move<0x128>(x));  // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float groups_sum(float x) {
+  x = x + dpp_move<0x128>(x);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Merges the 8 lane groups: afterwards every group holds the (m, l, acc) of
+// all the tokens the wave has seen.
+template <int HPW, int DPL>
+__device__ __forceinline__ void merge_groups(HeadState<HPW, DPL>& st) {
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    const float M = groups_max(st.m[h]);
+    const float f = exp2_fast(st.m[h] - M);
+    st.l[h] = groups_sum(st.l[h] * f);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) st.acc[h][e] = groups_sum(st.acc[h][e] * f);
+    st.m[h] = M;
+  }
+}
+
+// Streams blocks [j_begin, j_end) of sequence b through the online softmax of
+// query heads h0 .. h0 + HPW - 1, which all read KV head g; tokens at or past
+// t_end carry no weight.  Block ids are read 64 at a time, one per lane, and
+// broadcast with readlane.  On return the lane groups are merged.
+template <bool BF16, int D, int HPW, int NBUF, bool PBF16>
+__device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, int g, int h0,
+                                       int j_begin, int j_end, int t_end,
+                                       HeadState<HPW, D / 8>& st) {
+  uint32_t qv[HPW][RowShape<BF16, D>::W];
+  load_query<BF16, D, HPW>(a, lane, b, h0, qv);
+  reset_state(st);
+  const float sl2 = a.scale * kLog2e;
+  const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
+  Frag<BF16, D> buf[NBUF];
+
+  for (int c0 = j_begin; c0 < j_end; c0 += kMaxPartitionBlocks) {
+    const int nblk = min(kMaxPartitionBlocks, j_end - c0);
+    const int my_id = lane < nblk ? trow[c0 + lane] : -1;
+    // Block id and valid tokens of block jj of this run of ids: 0 tokens
+    // past the run's last block and for a table entry outside the pool.
+    auto block_of = [&](int jj, int& nvalid) __attribute__((always_inline)) {
+      const int blk = __builtin_amdgcn_readlane(my_id, jj & (kWave - 1));
+      const bool ok = jj < nblk && blk >= 0 && blk < a.num_blocks;
+      nvalid = ok ? min(kBlockTokens, t_end - (c0 + jj) * kBlockTokens) : 0;
+      return blk;
+    };
+    // Refills are unconditional: a block past the end gets a zero-length
+    // resource, so its loads touch no memory and keep the buffers in place.
+#pragma unroll
+    for (int s0 = 0; s0 < NBUF; ++s0) {
+      int nv;
+      const int blk = block_of(s0, nv);
+      load_block<BF16, D>(buf[s0], a, lane, g, blk, nv);
+    }
+    for (int base = 0; base < nblk; base += NBUF) {
+#pragma unroll
+      for (int s0 = 0; s0 < NBUF; ++s0) {
+        const int jj = base + s0;
+        if (jj < nblk) {
+          int nv;
+          block_of(jj, nv);
+          softmax_block<BF16, D, HPW, PBF16>(buf[s0], qv, lane, nv, sl2, st);
+        }
+        int nv;
+        const int blk = block_of(jj + NBUF, nv);
+        load_block<BF16, D>(buf[s0], a, lane, g, blk, nv);
+      }
+    }
+  }
+  merge_groups(st);
+}
+
+// After merge_groups every lane group holds all heads; lane group h (< HPW)
+// writes query head h0 + h to workspace slot slot0 + h * stride (slot =
+// (b * H_q + head) * P + piece).  The group's values are picked with selects,
+// so all stores sit under one branch.
+template <bool BF16, int D, int HPW>
+__device__ __forceinline__ void write_partial(const PagedLaunch& a, int lane, size_t slot0,
+                                              size_t stride, const HeadState<HPW, D / 8>& st) {
+  using S = RowShape<BF16, D>;
+  constexpr int DPL = S::DPL;
+  const int grp = lane >> 3;
+  const int sub = lane & 7;
+  float vals[DPL];
+  float mv = st.m[0], lv = st.l[0];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) vals[e] = st.acc[0][e];
+#pragma unroll
+  for (int h = 1; h < HPW; ++h) {
+    const bool mine = grp == h;
+    mv = mine ? st.m[h] : mv;
+    lv = mine ? st.l[h] : lv;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) vals[e] = mine ? st.acc[h][e] : vals[e];
+  }
+  if (grp < HPW) {
+    const size_t slot = slot0 + grp * stride;
+    float* orow = a.ws_o + slot * D;
+    // Chunk c of the lane is CW * EPW consecutive dimensions from
+    // (8 c + sub) CW EPW: 16-byte stores.
+    constexpr int RUN = S::CW * S::EPW;
+    static_assert(RUN % 4 == 0, "vector stores");
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+      for (int v = 0; v < RUN / 4; ++v) {
+        const float* x = &vals[c * RUN + 4 * v];
+        *reinterpret_cast<float4*>(orow + (c * 8 + sub) * RUN + 4 * v) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+    if (sub == 0) {
+      float2 ml;
+      ml.x = mv;
+      ml.y = lv;
+      reinterpret_cast<float2*>(a.ws_ml)[slot] = ml;
+    }
+  }
+}
+
+// Blocks of sequence b that hold positions (lengths clamped to max_seq_len).
+__device__ __forceinline__ int seq_blocks(const PagedLaunch& a, int b) {
+  const int len = min(a.seq_lens[b], a.max_seq_len);
+  return len > 0 ? (len + kBlockTokens - 1) / kBlockTokens : 0;
+}
+
 // NBUF: register buffers per wave (NBUF - 1 blocks in flight during compute).
 // WPE: waves per SIMD the register allocation is sized for.
-// WG: wavefronts per workgroup.  Consecutive units are the KV heads (and head
-// chunks) of one (sequence, partition), so a workgroup's waves read the same
-// blocks together: for 8 KV heads an 8-wave workgroup reads whole contiguous
-// token rows of every block.
 // PBF16: softmax weights enter the V product as bf16 pairs (dot2, fp32
 // accumulation) instead of fp32 FMAs; only for bf16 caches.
+//
+// Fixed partitions: one wavefront per unit (b, partition, kv head g, chunk of
+// HPW query heads).  WG: wavefronts per workgroup.  Consecutive units are the
+// KV heads (and head chunks) of one (sequence, partition), so a workgroup's
+// waves read the same blocks together: for 8 KV heads an 8-wave workgroup
+// reads whole contiguous token rows of every block.
 template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_partials_kernel(PagedLaunch a) {
-  static_assert(BF16 || !PBF16, "bf16 weights need a bf16 cache");
-  using S = RowShape<BF16, D>;
-  constexpr int W = S::W, CW = S::CW, NCH = S::NCH, RW = S::RW, DPL = S::DPL;
-
   const int lane = threadIdx.x & (kWave - 1);
-  const int grp = lane >> 3;
-  const int sub = lane & 7;
   const int ratio = a.num_q_heads / a.num_kv_heads;
   const int hchunks = ratio / HPW;
 
@@ -87,211 +380,119 @@ void paged_partials_kernel(PagedLaunch a) {
 
   int len = a.seq_lens[b];
   len = min(len, a.max_seq_len);
-  len = min(len, a.max_blocks_per_seq * kBlockTokens);
   const int t_begin = p * a.partition_tokens;
   if (len <= t_begin) return;
   const int t_end = min(len, t_begin + a.partition_tokens);
-  const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
   const int j0 = t_begin / kBlockTokens;
-
-  const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq + j0;
-  const int my_id = lane < nblk ? trow[lane] : -1;
-
+  const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
   const int h0 = g * ratio + hc * HPW;
-  const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
-                       (static_cast<size_t>(b) * a.num_q_heads + h0) * RW;
-  // Query slice of each head, in the same lane layout as the K rows.
-  uint32_t qv[HPW][W];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      load_words<CW>(&qv[h][c * CW], qw + h * RW + S::chunk_word(c, sub));
 
-  float m[HPW], l[HPW], acc[HPW][DPL];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    m[h] = kMinusBig;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-  }
-
-  const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * RW;  // words per token
-  const float sl2 = a.scale * kLog2e;
-  // Byte offset, inside a physical block, of the lane's chunk 0 for its two
-  // token slots (tokens grp and grp + 8); the same for every block.
-  uint32_t lane_off[2];
-#pragma unroll
-  for (int tok = 0; tok < 2; ++tok)
-    lane_off[tok] = static_cast<uint32_t>(((grp + 8 * tok) * tok_stride + g * RW +
-                                           S::chunk_word(0, sub)) * 4);
-  const uint32_t* kcache = static_cast<const uint32_t*>(a.k_cache);
-  const uint32_t* vcache = static_cast<const uint32_t*>(a.v_cache);
-
-  struct Frag {
-    uint32_t k[2][W];
-    uint32_t v[2][W];
-  };
-  Frag buf[NBUF];
-
-  // Tokens of block jj that hold data: 0 past the partition's last block and
-  // for a table entry outside the pool.
-  auto valid_tokens = [&](int jj, int& blk) __attribute__((always_inline)) {
-    blk = __builtin_amdgcn_readlane(my_id, jj & (kWave - 1));
-    const bool ok_blk = jj < nblk && blk >= 0 && blk < a.num_blocks;
-    const int tb = t_begin + jj * kBlockTokens;
-    return ok_blk ? min(kBlockTokens, t_end - tb) : 0;
-  };
-
-  // One buffer resource per block and tensor, whose record count ends after
-  // the block's last valid token: rows past it read back as zeros, so the
-  // unused tail of a sequence's last block (allocated, contents arbitrary)
-  // and out-of-pool table entries contribute nothing.
-  auto load_block = [&](Frag& f, int jj) __attribute__((always_inline)) {
-    int blk;
-    const int nvalid = valid_tokens(jj, blk);
-    const size_t base = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens * tok_stride;
-    const int bytes = nvalid * static_cast<int>(tok_stride) * 4;
-    const BufRsrc rk = make_rsrc(kcache + base, bytes);
-    const BufRsrc rv = make_rsrc(vcache + base, bytes);
-#pragma unroll
-    for (int tok = 0; tok < 2; ++tok)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        buffer_load_words<CW>(&f.k[tok][c * CW], rk, lane_off[tok] + c * 8 * CW * 4);
-        buffer_load_words<CW>(&f.v[tok][c * CW], rv, lane_off[tok] + c * 8 * CW * 4);
-      }
-  };
-
-  auto compute_block = [&](const Frag& f, int jj) __attribute__((always_inline)) {
-    int blk;
-    const int nvalid = valid_tokens(jj, blk);
-    float s[2][HPW];
-#pragma unroll
-    for (int tok = 0; tok < 2; ++tok) {
-      const bool ok = grp + 8 * tok < nvalid;
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) {
-        float part = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          if constexpr (BF16) {
-            part = dot2_bf16(qv[h][w], f.k[tok][w], part);
-          } else {
-            part = fmaf(__uint_as_float(qv[h][w]), __uint_as_float(f.k[tok][w]), part);
-          }
-        }
-        const float z = sum_over_8(part) * sl2;
-        s[tok][h] = ok ? z : -INFINITY;
-      }
-    }
-    // Rows past the valid tokens were read as zeros: weight 0 times value 0.
-    const uint32_t (&vw)[2][W] = f.v;
-    // For bf16 weights: the V elements of the lane's two tokens, paired per
-    // dimension (shared by all heads of the group).
-    uint32_t vlo[PBF16 ? W : 1], vhi[PBF16 ? W : 1];
-    if constexpr (PBF16) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        vlo[w] = pair_lo(vw[0][w], vw[1][w]);
-        vhi[w] = pair_hi(vw[0][w], vw[1][w]);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      const float mx = fmaxf(s[0][h], s[1][h]);
-      const bool up = mx > m[h] + kRaise;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float mn = up ? mx : m[h];
-        const float alpha = exp2_fast(m[h] - mn);
-        l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
-        m[h] = mn;
-      }
-      const float p0 = exp2_fast(s[0][h] - m[h]);
-      const float p1 = exp2_fast(s[1][h] - m[h]);
-      if constexpr (PBF16) {
-        // Weights rounded to bf16 and paired over the lane's two tokens; the
-        // same rounded weights feed the sum, so the output stays an exact
-        // convex combination of V rows.  Products accumulate in fp32.
-        const uint32_t pp = pack_bf16x2(p0, p1);
-        l[h] = dot2_bf16(pp, kBf16OnePair, l[h]);
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          acc[h][2 * w] = dot2_bf16(pp, vlo[w], acc[h][2 * w]);
-          acc[h][2 * w + 1] = dot2_bf16(pp, vhi[w], acc[h][2 * w + 1]);
-        }
-      } else {
-        l[h] += p0 + p1;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-          if constexpr (BF16) {
-            acc[h][2 * w] = fmaf(p1, bf16_lo(vw[1][w]), fmaf(p0, bf16_lo(vw[0][w]), acc[h][2 * w]));
-            acc[h][2 * w + 1] = fmaf(p1, bf16_hi(vw[1][w]), fmaf(p0, bf16_hi(vw[0][w]), acc[h][2 * w + 1]));
-          } else {
-            acc[h][w] = fmaf(p1, __uint_as_float(vw[1][w]), fmaf(p0, __uint_as_float(vw[0][w]), acc[h][w]));
-          }
-        }
-      }
-    }
-  };
-
-  // Refills are unconditional: a block past the end gets a zero-length
-  // resource, so its loads touch no memory and keep the buffers in place.
-#pragma unroll
-  for (int s0 = 0; s0 < NBUF; ++s0) load_block(buf[s0], s0);
-  for (int base = 0; base < nblk; base += NBUF) {
-#pragma unroll
-    for (int s0 = 0; s0 < NBUF; ++s0) {
-      const int jj = base + s0;
-      if (jj < nblk) compute_block(buf[s0], jj);
-      load_block(buf[s0], jj + NBUF);
-    }
-  }
-
-  // Merge the 8 lane groups (lanes differing in bits 3..5).
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    float M = m[h];
-    M = fmaxf(M, shfl_xor_f(M, 8));
-    M = fmaxf(M, shfl_xor_f(M, 16));
-    M = fmaxf(M, shfl_xor_f(M, 32));
-    const float f = exp2_fast(m[h] - M);
-    float lt = l[h] * f;
-    lt += shfl_xor_f(lt, 8);
-    lt += shfl_xor_f(lt, 16);
-    lt += shfl_xor_f(lt, 32);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      float x = acc[h][e] * f;
-      x += shfl_xor_f(x, 8);
-      x += shfl_xor_f(x, 16);
-      x += shfl_xor_f(x, 32);
-      acc[h][e] = x;
-    }
-    m[h] = M;
-    l[h] = lt;
-  }
-
-  // Group k writes query head h0 + k.
+  HeadState<HPW, D / 8> st;
+  attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + nblk, t_end, st);
   const size_t P = a.num_partitions;
+  write_partial<BF16, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P, st);
+}
+
+// Balanced split (automatic mode).  The work list is every (sequence b,
+// unit group ug, block j) in that order, a unit group being WG consecutive
+// units (KV head, head chunk); wave w of a workgroup does unit ug * WG + w, so
+// the workgroup's waves read the same block rows together.  Workgroup k takes
+// list items [k per, (k + 1) per) with per = max(kMinPieceBlocks, ceil(total /
+// workgroups)) and as many workgroups as are resident at once: every compute
+// unit streams the same number of blocks whatever the length mix.  Its waves
+// walk the items as segments of one (b, ug) each; at a segment's end each
+// wave writes the partial result of its unit's heads as piece (k - first
+// workgroup of the segment), and the workgroup of piece 0 records the number
+// of pieces for the merge.  Pieces of one (b, h) never exceed ceil(blocks /
+// kMinPieceBlocks) + 1.
+template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
+__global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void paged_balanced_kernel(PagedLaunch a) {
+  extern __shared__ int blk_prefix[];  // [batch + 1]: blocks of the sequences before b
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int ratio = a.num_q_heads / a.num_kv_heads;
+  const int hchunks = ratio / HPW;
+  const int units = a.num_kv_heads * hchunks;
+  const int n_ug = (units + WG - 1) / WG;
+
+  if (wave == 0) {
+    int run = 0;
+    for (int c = 0; c < a.batch; c += kWave) {
+      int x = c + lane < a.batch ? seq_blocks(a, c + lane) : 0;
 #pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    if (grp == h) {
-      const size_t slot = (static_cast<size_t>(b) * a.num_q_heads + h0 + h) * P + p;
-      float* orow = a.ws_o + slot * D;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) orow[S::dim_of(e, sub)] = acc[h][e];
-      if (sub == 0) {
-        float2 ml;
-        ml.x = m[h];
-        ml.y = l[h];
-        reinterpret_cast<float2*>(a.ws_ml)[slot] = ml;
+      for (int sh = 1; sh < kWave; sh <<= 1) {
+        const int y = __shfl_up(x, sh, kWave);
+        if (lane >= sh) x += y;
       }
+      if (c + lane < a.batch) blk_prefix[c + lane + 1] = run + x;
+      run += __shfl(x, kWave - 1, kWave);
+    }
+    if (lane == 0) blk_prefix[0] = 0;
+  }
+  __syncthreads();
+
+  // Prefix reads are wave-uniform; readfirstlane tells the compiler, which
+  // would otherwise keep the segment state in VGPRs under masked branches.
+  auto prefix = [&](int i) __attribute__((always_inline)) { return wave_uniform(blk_prefix[i]); };
+  const int total = n_ug * prefix(a.batch);
+  const int per = max(kMinPieceBlocks, (total + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x));
+  const int wg = blockIdx.x;
+  int item = wg * per;
+  if (item >= total) return;  // whole workgroup
+  const int end = min(total, item + per);
+
+  // Sequence of the first item: the last b whose items start at or before it
+  // (never an empty sequence, whose start equals its successor's).
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (n_ug * prefix(mid) <= item) lo = mid; else hi = mid - 1;
+  }
+  int b = lo;
+
+  const size_t P = a.num_partitions;
+  HeadState<HPW, D / 8> st;
+  while (item < end) {
+    const int pb = prefix(b);
+    const int nb = prefix(b + 1) - pb;
+    const int base = n_ug * pb;
+    const int ug = (item - base) / nb;
+    const int j0 = item - base - ug * nb;
+    const int seg_begin = base + ug * nb;
+    const int seg_end = min(end, seg_begin + nb);
+    const int u = ug * WG + wave;
+    if (u < units) {
+      const int g = u / hchunks, hc = u % hchunks;
+      const int h0 = g * ratio + hc * HPW;
+      const int t_end = wave_uniform(min(a.seq_lens[b], a.max_seq_len));
+      attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st);
+      const int first = seg_begin / per;
+      const int piece = wg - first;
+      const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
+      write_partial<BF16, D, HPW>(a, lane, row0 * P + piece, P, st);
+      if (piece == 0 && lane < HPW) a.counts[row0 + lane] = (seg_begin + nb - 1) / per - first + 1;
+    }
+    item = seg_end;
+    if (item == base + n_ug * nb) {
+      ++b;
+      while (b < a.batch && prefix(b + 1) == prefix(b)) ++b;
     }
   }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = BF16>
@@ -305,6 +506,17 @@ hipError_t launch_variant(const PagedLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Balanced split: as many workgroups as are resident at once (4 * WPE
+// wavefronts per compute unit, in workgroups of WG waves).
+template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = BF16>
+hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(a.batch + 1) * sizeof(int);
+  const int groups = device_cus() * ((4 * WPE) / WG);
+  hipLaunchKernelGGL((paged_balanced_kernel<BF16, D, HPW, NBUF, WPE, WG, PBF16>),
+                     dim3(static_cast<unsigned>(groups)), dim3(64 * WG), lds, stream, a);
+  return hipGetLastError();
+}
+
 // Tuned on MI355X (bf16, d_head 128): one head per wave keeps 3 waves per
 // SIMD; four heads per wave need ~200 VGPRs (2 waves per SIMD) and do best
 // with two buffers.  Eight-wave workgroups help when a group's rows are read
@@ -315,6 +527,11 @@ hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
   constexpr int NBUF = (BF16 && HPW == 1) ? 3 : 2;
   constexpr int WPE = (HPW == 1 && kWide) ? 3 : (kWide ? 2 : 1);
   const int ratio = a.num_q_heads / a.num_kv_heads;
+  if (a.counts) {
+    // Whole workgroups must fill the 4 * WPE wave slots of a compute unit.
+    if constexpr ((4 * WPE) % 8 == 0) return launch_balanced<BF16, D, HPW, NBUF, WPE, 8>(a, stream);
+    return launch_balanced<BF16, D, HPW, NBUF, WPE, 4>(a, stream);
+  }
   if constexpr (kWide) {
     if (HPW == 1 || ratio > HPW) return launch_variant<BF16, D, HPW, NBUF, WPE, 8>(a, stream);
   }

@@ -12,13 +12,20 @@ namespace kvd {
 // Workspace of the split decode: per (b, h, partition) an fp32 output row of
 // head_dim values, then per (b, h, partition) the pair (max, sum).  The max is
 // kept in log2 units (scores are pre-multiplied by log2 e).
+// With the balanced split P is the bound on the pieces of one (b, h) and a
+// third array holds, per (b, h), the number of pieces written.
 struct WorkspaceLayout {
-  size_t o_bytes;   // [B, H_q, P, D] fp32
-  size_t ml_offset; // start of [B, H_q, P] float2, 256-B aligned
+  size_t o_bytes;        // [B, H_q, P, D] fp32
+  size_t ml_offset;      // start of [B, H_q, P] float2, 256-B aligned
+  size_t counts_offset;  // start of [B, H_q] int32 piece counts (balanced split only)
   size_t total;
 };
 
-WorkspaceLayout workspace_layout(int batch, int num_q_heads, int num_partitions, int head_dim);
+WorkspaceLayout workspace_layout(int batch, int num_q_heads, int num_partitions, int head_dim,
+                                 bool balanced);
+
+// Smallest piece of the balanced split, in 16-token blocks.
+constexpr int kBalancedMinPieceBlocks = 16;
 
 struct PagedLaunch {
   const void* q;
@@ -33,6 +40,7 @@ struct PagedLaunch {
   int partition_tokens, num_partitions;
   float scale;
   bool bf16;
+  int* counts;  // balanced split: piece counts per (b, h); NULL for fixed partitions
 };
 
 struct MergeLaunch {
@@ -44,6 +52,7 @@ struct MergeLaunch {
   int max_blocks_per_seq_tokens;  // clamp bound for seq_lens (max_seq_len)
   int partition_tokens, num_partitions;
   bool bf16;
+  const int* counts;  // balanced split: piece counts per (b, h); NULL for fixed partitions
 };
 
 struct AppendLaunch {

@@ -45,11 +45,28 @@ def test_workspace_layout():
     assert kvd.decode_attn_workspace_bytes(B, Hq, Hkv, D, L, pt) == pad(o) + pad(ml)
 
 
+def test_balanced_workspace_layout():
+    # Automatic mode of the paged path: at most ceil(ceil(L / 16) / 16) + 1
+    # pieces per (b, h), then an int32 piece count per (b, h), each section
+    # padded to 256 B.
+    B, Hq, Hkv, D, L = 3, 8, 2, 128, 1000
+    P = -(-(-(-L // 16)) // 16) + 1
+    pad = lambda x: -(-x // 256) * 256  # noqa: E731
+    want = pad(B * Hq * P * D * 4) + pad(B * Hq * P * 2 * 4) + pad(B * Hq * 4)
+    assert kvd.decode_attn_workspace_bytes(B, Hq, Hkv, D, L, 0) == want
+
+
 def test_partition_choice():
     assert kvd.decode_attn_partition_tokens(4, 64, 8, 128, 131072, 512) == 512
-    auto = kvd.decode_attn_partition_tokens(64, 32, 8, 128, 8192, 0)
+    # 0 = balanced split for the paged path
+    assert kvd.decode_attn_partition_tokens(64, 32, 8, 128, 8192, 0) == 0
+    assert kvd.decode_attn_partition_tokens(1, 4, 4, 32, 129, 0) == 0
+    # the latent (MLA) path keeps fixed partitions: one workgroup per CU
+    assert kvd.decode_attn_partition_tokens(32, 128, 1, 512, 4096, 0) == 1024
+    assert kvd.decode_attn_partition_tokens(1, 128, 1, 512, 4096, 0) == 64
+    # batches beyond the balanced split's limit fall back to fixed partitions
+    auto = kvd.decode_attn_partition_tokens(20000, 32, 8, 128, 1024, 0)
     assert auto % 16 == 0 and 64 <= auto <= 1024
-    assert kvd.decode_attn_partition_tokens(1, 4, 4, 32, 129, 0) == 64
     with pytest.raises(kvd.KvdError):
         kvd.decode_attn_partition_tokens(1, 4, 4, 32, 129, 24)
     with pytest.raises(kvd.KvdError):

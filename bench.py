@@ -304,6 +304,8 @@ def main():
 
     kv_bytes = inp.kv_bytes_read
     step_s = ms_step / 1e3
+    # The automatic mode (partition 0) runs the balanced split.
+    kernel = "paged_balanced" if pt_used == 0 else "paged_partials"
     value = kv_bytes / step_s / 1e9
     achieved = kv_bytes / (part_avg / 1e3) / 1e9
 
@@ -330,10 +332,10 @@ def main():
         "wall_s_timed": round(wall, 4),
         "kernel_ms": {"partials_avg": round(part_avg, 5), "partials_min": round(min(part_ms), 5),
                       "partials_max": round(max(part_ms), 5)},
-        "roofline": {"bound": "hbm", "kernel": "paged_partials_kernel",
+        "roofline": {"bound": "hbm", "kernel": kernel + "_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("paged_partials", args.workload)},
+                     "traffic": recorded_traffic(kernel, args.workload)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

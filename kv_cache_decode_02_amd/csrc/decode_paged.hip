@@ -39,6 +39,12 @@ namespace {
 constexpr float kRaise = 8.0f;
 constexpr int kMaxPartitionBlocks = 64;  // one block id per lane
 constexpr int kMinPieceBlocks = kBalancedMinPieceBlocks;
+// Relative share of a workgroup on an even and an odd XCD (workgroup k runs
+// on XCD k mod 8).  Measured on MI355X with the GQA decode batch: streaming
+// the same number of blocks takes the odd XCDs about 6% longer, on every
+// repetition and on different boards, so the even ones get 6% more.
+constexpr long long kEvenXcdShare = 1059;
+constexpr long long kOddXcdShare = 1000;
 
 template <bool BF16, int D>
 struct RowShape {
@@ -396,14 +402,18 @@ void paged_partials_kernel(PagedLaunch a) {
 // Balanced split (automatic mode).  The work list is every (sequence b,
 // unit group ug, block j) in that order, a unit group being WG consecutive
 // units (KV head, head chunk); wave w of a workgroup does unit ug * WG + w, so
-// the workgroup's waves read the same block rows together.  Workgroup k takes
-// list items [k per, (k + 1) per) with per = max(kMinPieceBlocks, ceil(total /
-// workgroups)) and as many workgroups as are resident at once: every compute
-// unit streams the same number of blocks whatever the length mix.  Its waves
-// walk the items as segments of one (b, ug) each; at a segment's end each
-// wave writes the partial result of its unit's heads as piece (k - first
-// workgroup of the segment), and the workgroup of piece 0 records the number
-// of pieces for the merge.  Pieces of one (b, h) never exceed ceil(blocks /
+// the workgroup's waves read the same block rows together.  As many
+// workgroups as are resident at once each take one contiguous share of the
+// list, [bound(k), bound(k + 1)), whatever the length mix: shares are
+// proportional to kEvenXcdShare / kOddXcdShare by the parity of the
+// workgroup's XCD, so that all finish together; when the list is short
+// (fewer than kMinPieceBlocks + 1 items per workgroup) the shares are equal,
+// kMinPieceBlocks long, and the last workgroups have none.  Every share is
+// at least kMinPieceBlocks items but the last.  The waves walk their share as
+// segments of one (b, ug) each; at a segment's end each wave writes the
+// partial result of its unit's heads as piece (k - the workgroup holding the
+// segment's first item), and the workgroup of piece 0 records the number of
+// pieces for the merge.  Pieces of one (b, h) never exceed ceil(blocks /
 // kMinPieceBlocks) + 1.
 template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
@@ -436,11 +446,30 @@ void paged_balanced_kernel(PagedLaunch a) {
   // would otherwise keep the segment state in VGPRs under masked branches.
   auto prefix = [&](int i) __attribute__((always_inline)) { return wave_uniform(blk_prefix[i]); };
   const int total = n_ug * prefix(a.batch);
-  const int per = max(kMinPieceBlocks, (total + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x));
+  const int groups = gridDim.x;
   const int wg = blockIdx.x;
-  int item = wg * per;
-  if (item >= total) return;  // whole workgroup
-  const int end = min(total, item + per);
+  const bool weighted = total >= groups * (kMinPieceBlocks + 1);
+  const int per = max(kMinPieceBlocks, (total + groups - 1) / groups);  // equal shares
+  // Weight of the first k workgroups (even ones: indices 0, 2, 4, ...).
+  auto weight = [&](int k) __attribute__((always_inline)) {
+    return kEvenXcdShare * ((k + 1) / 2) + kOddXcdShare * (k / 2);
+  };
+  const long long wsum = weight(groups);
+  auto bound = [&](int k) __attribute__((always_inline)) {
+    return weighted ? static_cast<int>(static_cast<long long>(total) * weight(k) / wsum)
+                    : min(total, k * per);
+  };
+  // Workgroup whose share holds item x.
+  auto owner = [&](int x) __attribute__((always_inline)) {
+    if (!weighted) return x / per;
+    int k = static_cast<int>(static_cast<long long>(x) * groups / total);
+    while (k + 1 < groups && bound(k + 1) <= x) ++k;
+    while (k > 0 && bound(k) > x) --k;
+    return k;
+  };
+  int item = bound(wg);
+  const int end = bound(wg + 1);
+  if (item >= end) return;  // whole workgroup
 
   // Sequence of the first item: the last b whose items start at or before it
   // (never an empty sequence, whose start equals its successor's).
@@ -467,11 +496,11 @@ void paged_balanced_kernel(PagedLaunch a) {
       const int h0 = g * ratio + hc * HPW;
       const int t_end = wave_uniform(min(a.seq_lens[b], a.max_seq_len));
       attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st);
-      const int first = seg_begin / per;
+      const int first = owner(seg_begin);
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
       write_partial<BF16, D, HPW>(a, lane, row0 * P + piece, P, st);
-      if (piece == 0 && lane < HPW) a.counts[row0 + lane] = (seg_begin + nb - 1) / per - first + 1;
+      if (piece == 0 && lane < HPW) a.counts[row0 + lane] = owner(seg_begin + nb - 1) - first + 1;
     }
     item = seg_end;
     if (item == base + n_ug * nb) {

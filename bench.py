@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4,
                     help="MLA: rotate over this many copies of the latent cache so the "
                          "timed reads come from HBM, not the 256 MB Infinity Cache")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of a captured HIP graph of the step")
     ap.add_argument("--partition", type=int, default=-1,
                     help="partition tokens (-1: the workload's own, 0: library auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -85,6 +87,43 @@ def up(a, dev):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     return torch.from_numpy(a).to(dev)
+
+
+def time_graph(torch, step, out, args):
+    """Capture one step (append, partials, merge) in a HIP graph, check that
+    replays give the eager step's output bit for bit (with eager work between
+    replays), then time args.steps replays.  Returns (ms per step, True)."""
+    stream = torch.cuda.current_stream()
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()  # first run on the capture stream outside the capture
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay differs from the eager step")
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / args.steps, True
 
 
 def recorded_traffic(kernel, workload):
@@ -290,6 +329,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Eager steps, with events around the partials kernel (the roofline).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -301,9 +341,12 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_eager = start.elapsed_time(end) / args.steps
     part_ms = [a.elapsed_time(b) for a, b in evs]
     part_avg = float(np.mean(part_ms))
+    ms_step, graph_check = ms_eager, None
+    if not args.no_graph:
+        ms_step, graph_check = time_graph(torch, step, out, args)
 
     kv_bytes = inp.kv_bytes_read
     step_s = ms_step / 1e3
@@ -324,6 +367,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": inp.dtype,
+        "step_launch": "hip graph" if not args.no_graph else "eager",
+        "ms_per_step_eager": round(ms_eager, 5),
+        "graph_replays_match_eager": graph_check,
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": H_q,
                    "num_kv_heads": H_kv, "head_dim": d, "block_size": 16,

@@ -15,12 +15,21 @@
 namespace kvd {
 namespace {
 
-template <bool BF16, int D>
+// WPB wavefronts per (b, h): one (four (b, h) per 256-thread workgroup) when
+// a (b, h) has few pieces, four (one (b, h) per workgroup) when it may have
+// many; the waves of one (b, h) take every WPB-th run of 64 slots and add
+// their sums through LDS.  Rows of the non-empty slots are read kRows at a
+// time.
+template <bool BF16, int D, int WPB>
 __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
   constexpr int DL = D >= kWave ? D / kWave : 1;  // dims per lane
+  constexpr int kRows = 8;
+  __shared__ float red[WPB][D + 2];
   const int lane = threadIdx.x & (kWave - 1);
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= a.batch * a.num_q_heads) return;
+  const int wave = threadIdx.x >> 6;
+  const int sw = wave % WPB;  // this wave's part of the (b, h)
+  const int bh = blockIdx.x * (4 / WPB) + wave / WPB;
+  if (bh >= a.batch * a.num_q_heads) return;  // with WPB > 1 the whole workgroup
   const int b = bh / a.num_q_heads;
 
   int len = a.seq_lens[b];
@@ -31,44 +40,50 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + bh * P;
   const float* o = a.ws_o + bh * P * D;
 
-  // Pass 1, lanes over slots: the common maximum.  Slots with l = 0 (empty
-  // markers of the streamed split, or pieces without valid tokens) carry no
-  // weight and are skipped.
+  // Pass 1, lanes over slots: the common maximum.  Slots with l = 0 (pieces
+  // without valid tokens) carry no weight and are skipped.
   float M = kMinusBig;
-  for (int p = lane; p < np; p += kWave) {
+  for (int p = sw * kWave + lane; p < np; p += kWave * WPB) {
     const float2 v = ml[p];
     if (v.y > 0.f) M = fmaxf(M, v.x);
   }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
+  if constexpr (WPB > 1) {
+    if (lane == 0) red[sw][D] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) M = fmaxf(M, red[w][D]);
+    __syncthreads();
+  }
 
-  // Pass 2: 64 slots at a time, the non-empty ones from a ballot; their
-  // weights come from the owning lane, their rows are read 4 at a time.
+  // Pass 2: runs of 64 slots; the non-empty ones from a ballot, their weights
+  // from the owning lane, their rows kRows at a time.
   const bool active = lane * DL < D;
   float acc[DL];
 #pragma unroll
   for (int d = 0; d < DL; ++d) acc[d] = 0.f;
   float den = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kWave) {
+  for (int p0 = sw * kWave; p0 < np; p0 += kWave * WPB) {
     const float2 v = p0 + lane < np ? ml[p0 + lane] : make_float2(kMinusBig, 0.f);
     const float w_lane = v.y > 0.f ? exp2_fast(v.x - M) : 0.f;
     den += w_lane * v.y;
     uint64_t mask = __builtin_amdgcn_ballot_w64(v.y > 0.f);
     while (mask) {
-      int idx[4];
+      int idx[kRows];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kRows; ++k) {
         idx[k] = mask ? static_cast<int>(__builtin_ctzll(mask)) : -1;
         mask &= mask - 1;
       }
-      float rows[4][DL];
+      float rows[kRows][DL];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < kRows; ++k)
 #pragma unroll
         for (int d = 0; d < DL; ++d)
           rows[k][d] = (idx[k] >= 0 && active) ? o[(p0 + idx[k]) * D + lane * DL + d] : 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kRows; ++k) {
         const float w = __shfl(w_lane, idx[k] >= 0 ? idx[k] : 0, kWave);
         if (idx[k] >= 0) {
 #pragma unroll
@@ -79,6 +94,26 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
   }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) den += shfl_xor_f(den, s);
+  if constexpr (WPB > 1) {
+    if (active) {
+#pragma unroll
+      for (int d = 0; d < DL; ++d) red[sw][lane * DL + d] = acc[d];
+    }
+    if (lane == 0) red[sw][D + 1] = den;
+    __syncthreads();
+    if (sw != 0) return;
+    if (active) {
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        float x = acc[d];
+#pragma unroll
+        for (int w = 1; w < WPB; ++w) x += red[w][lane * DL + d];
+        acc[d] = x;
+      }
+    }
+#pragma unroll
+    for (int w = 1; w < WPB; ++w) den += red[w][D + 1];
+  }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   if (active) {
     if constexpr (BF16) {
@@ -93,17 +128,24 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
   }
 }
 
-template <bool BF16>
-hipError_t launch_merge_typed(const MergeLaunch& a, hipStream_t stream) {
+template <bool BF16, int WPB>
+hipError_t launch_merge_waves(const MergeLaunch& a, hipStream_t stream) {
   const long long bh = static_cast<long long>(a.batch) * a.num_q_heads;
-  const dim3 grid(static_cast<unsigned>((bh + 3) / 4));
+  const dim3 grid(static_cast<unsigned>((bh + (4 / WPB) - 1) / (4 / WPB)));
   switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL((merge_kernel<BF16, 32>), grid, dim3(256), 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((merge_kernel<BF16, 64>), grid, dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((merge_kernel<BF16, 128>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((merge_kernel<BF16, 512>), grid, dim3(256), 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((merge_kernel<BF16, 32, WPB>), grid, dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((merge_kernel<BF16, 64, WPB>), grid, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((merge_kernel<BF16, 128, WPB>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((merge_kernel<BF16, 512, WPB>), grid, dim3(256), 0, stream, a); break;
   }
   return hipGetLastError();
+}
+
+// Four waves per (b, h) once a (b, h) may hold more than 64 pieces.
+template <bool BF16>
+hipError_t launch_merge_typed(const MergeLaunch& a, hipStream_t stream) {
+  return a.num_partitions > 64 ? launch_merge_waves<BF16, 4>(a, stream)
+                               : launch_merge_waves<BF16, 1>(a, stream);
 }
 
 }  // namespace

@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4,
                     help="MLA: rotate over this many copies of the latent cache so the "
                          "timed reads come from HBM, not the 256 MB Infinity Cache")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="run kv_append_paged as its own kernel instead of fused into the attention pass")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of a captured HIP graph of the step")
     ap.add_argument("--partition", type=int, default=-1,
@@ -317,10 +319,19 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        kvd.kv_append_paged(kc, vc, kn, vn, table, seq)
+        # One decode step: append this step's K/V, attend, merge.  By default
+        # the append is fused into the attention pass (one kernel reads the
+        # history and writes the new rows); --separate-append runs
+        # kv_append_paged first.
+        if args.separate_append:
+            kvd.kv_append_paged(kc, vc, kn, vn, table, seq)
         if ev is not None:
             ev[0].record(stream)
-        kvd.decode_attn_paged_partials(q, kc, vc, table, seq, L, ws, partition_tokens=pt)
+        if args.separate_append:
+            kvd.decode_attn_paged_partials(q, kc, vc, table, seq, L, ws, partition_tokens=pt)
+        else:
+            kvd.decode_attn_paged_append_partials(q, kc, vc, kn, vn, table, seq, L, ws,
+                                                  partition_tokens=pt)
         if ev is not None:
             ev[1].record(stream)
         kvd.decode_attn_merge(out, seq, H_kv, L, ws, partition_tokens=pt)
@@ -368,6 +379,8 @@ def main():
         "vs_baseline": None,
         "dtype": inp.dtype,
         "step_launch": "hip graph" if not args.no_graph else "eager",
+        "step_kernels": ("kv_append_paged, partials, merge" if args.separate_append
+                         else "append fused into partials, merge"),
         "ms_per_step_eager": round(ms_eager, 5),
         "graph_replays_match_eager": graph_check,
         "data": "synthetic",

@@ -181,6 +181,44 @@ int decode_attn_merge(void* out, const int32_t* seq_lens, int batch, int num_q_h
                       void* stream);
 
 /*
+ * decode_attn_paged_append -- kv_append_paged followed by decode_attn_paged,
+ * in one pass over the cache: the decode step of "KV-Cache——为什么AI回复越来越
+ * 快" (02: this step's K/V join the cache, then the new query attends to all
+ * of it) and of "单请求 KV Cache" (生产系统的做法: preallocated in-place slot
+ * write).  Position seq_lens[b] - 1 takes its K/V from k_new / v_new (read
+ * once, used as the last token of the softmax) and the rows are written into
+ * their cache slot as kv_append_paged would write them; the other positions
+ * are read from the cache.  The result equals the two separate calls up to
+ * the order of floating-point accumulation.
+ *   k_new, v_new  [batch, num_kv_heads, head_dim] dtype, 16-byte aligned
+ *   k_cache, v_cache are written (the new rows' slots only)
+ * Other arguments, sizes, workspace and errors as for decode_attn_paged.
+ * Rows are written and used only for sequences with 1 <= seq_lens[b] <=
+ * max_seq_len whose last block is inside the pool (the preconditions of the
+ * separate calls); the block holding the new position must not be shared.
+ */
+int decode_attn_paged_append(void* out, const void* q, void* k_cache, void* v_cache,
+                             const void* k_new, const void* v_new, const int32_t* block_table,
+                             const int32_t* seq_lens, int batch, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                             float scale, int partition_tokens, void* workspace,
+                             size_t workspace_bytes, kvd_dtype_t dtype, void* stream);
+
+/*
+ * decode_attn_paged_append_partials -- first phase of decode_attn_paged_append
+ * only (same arguments minus `out`); finish with decode_attn_merge.
+ */
+int decode_attn_paged_append_partials(const void* q, void* k_cache, void* v_cache,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int max_seq_len, float scale, int partition_tokens,
+                                      void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                                      void* stream);
+
+/*
  * decode_attn_mla -- absorbed multi-head latent attention decode (bf16).
  *
  * The cache keeps one row per token: the latent c_t (d_c values) followed by

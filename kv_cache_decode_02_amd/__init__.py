@@ -2,7 +2,8 @@
 
 One decode step of one layer: ``kv_append_paged`` writes the step's K/V row
 into the paged cache, ``decode_attn_paged`` attends over the whole visible
-history (split-KV partials, then a log-sum-exp merge); ``decode_attn_mla`` is
+history (split-KV partials, then a log-sum-exp merge), and
+``decode_attn_paged_append`` does both in one pass; ``decode_attn_mla`` is
 the absorbed multi-head latent attention variant over a latent cache.  The functions mirror
 the C ABI in ``include/kvdecode.h`` and only marshal arguments; importing this
 package fails if the HIP library has not been built.
@@ -13,6 +14,8 @@ from ._native import (
     kv_append_paged,
     decode_attn_paged,
     decode_attn_paged_partials,
+    decode_attn_paged_append,
+    decode_attn_paged_append_partials,
     decode_attn_merge,
     decode_attn_workspace_bytes,
     decode_attn_partition_tokens,
@@ -26,6 +29,7 @@ from ._native import (
 
 __all__ = [
     "KvdError", "kv_append_paged", "decode_attn_paged", "decode_attn_paged_partials",
+    "decode_attn_paged_append", "decode_attn_paged_append_partials",
     "decode_attn_merge", "decode_attn_workspace_bytes", "decode_attn_partition_tokens",
     "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials", "mla_default_scale",
     "LIB_PATH", "HEADER_PATH",

@@ -45,6 +45,12 @@ lib.decode_attn_paged.restype = _i
 lib.decode_attn_paged.argtypes = [_vp] + _PAGED_ARGS
 lib.decode_attn_paged_partials.restype = _i
 lib.decode_attn_paged_partials.argtypes = _PAGED_ARGS
+# q, k_cache, v_cache, k_new, v_new, then the paged arguments from block_table on
+_APPEND_ARGS = _PAGED_ARGS[:3] + [_vp, _vp] + _PAGED_ARGS[3:]
+lib.decode_attn_paged_append.restype = _i
+lib.decode_attn_paged_append.argtypes = [_vp] + _APPEND_ARGS
+lib.decode_attn_paged_append_partials.restype = _i
+lib.decode_attn_paged_append_partials.argtypes = _APPEND_ARGS
 _MLA_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 lib.decode_attn_mla.restype = _i
 lib.decode_attn_mla.argtypes = [_vp] + _MLA_ARGS
@@ -182,6 +188,47 @@ def decode_attn_paged_partials(q, k_cache, v_cache, block_table, seq_lens, max_s
     args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
                        partition_tokens, workspace)
     _check(lib.decode_attn_paged_partials(*args, _stream(stream)), "decode_attn_paged_partials")
+
+
+def _append_args(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens, max_seq_len, scale,
+                 partition_tokens, ws):
+    args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+                       partition_tokens, ws)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, dtype=k_cache.dtype)
+        if tuple(t.shape) != (q.shape[0], k_cache.shape[2], k_cache.shape[3]):
+            raise KvdError(f"{n} must be [B, H_kv, d]")
+    return args[:3] + [_ptr(k_new), _ptr(v_new)] + args[3:]
+
+
+def decode_attn_paged_append(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens,
+                             max_seq_len, scale=None, partition_tokens=0, workspace=None,
+                             out=None, stream=None):
+    """kv_append_paged + decode_attn_paged in one pass: writes k_new / v_new
+    [B, H_kv, d] into their slots and attends over the history plus them."""
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    if workspace is None:
+        workspace = alloc_workspace(B, h_q, h_kv, d, max_seq_len, partition_tokens,
+                                    device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype)
+    args = _append_args(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens, max_seq_len,
+                        scale, partition_tokens, workspace)
+    _check(lib.decode_attn_paged_append(_ptr(out), *args, _stream(stream)),
+           "decode_attn_paged_append")
+    return out
+
+
+def decode_attn_paged_append_partials(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens,
+                                      max_seq_len, workspace, scale=None, partition_tokens=0,
+                                      stream=None):
+    """First phase of decode_attn_paged_append only (the append included)."""
+    args = _append_args(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens, max_seq_len,
+                        scale, partition_tokens, workspace)
+    _check(lib.decode_attn_paged_append_partials(*args, _stream(stream)),
+           "decode_attn_paged_append_partials")
 
 
 def decode_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_tokens=0,

@@ -239,6 +239,8 @@ static PagedLaunch paged_launch(const void* q, const void* k_cache, const void* 
   a.counts = s.balanced
                  ? reinterpret_cast<int*>(static_cast<char*>(workspace) + s.ws.counts_offset)
                  : nullptr;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   return a;
 }
 
@@ -322,6 +324,56 @@ int decode_attn_paged(void* out, const void* q, const void* k_cache, const void*
   const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
                                      workspace, dtype, s);
   return hip_status(launch_merge(m, st));
+}
+
+int decode_attn_paged_append_partials(const void* q, void* k_cache, void* v_cache,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int max_seq_len, float scale, int partition_tokens,
+                                      void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                                      void* stream) {
+  Sizes s;
+  const int rc = check_paged(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                             num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                             max_seq_len, partition_tokens, workspace, workspace_bytes, dtype, &s);
+  if (rc) return rc;
+  if (batch == 0) return KVD_OK;
+  if (!k_new || !v_new) return KVD_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVD_ERR_SHAPE;
+  PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                               num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
+                               max_seq_len, scale, workspace, dtype, s);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  return hip_status(launch_paged_partials(a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_paged_append(void* out, const void* q, void* k_cache, void* v_cache,
+                             const void* k_new, const void* v_new, const int32_t* block_table,
+                             const int32_t* seq_lens, int batch, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                             float scale, int partition_tokens, void* workspace,
+                             size_t workspace_bytes, kvd_dtype_t dtype, void* stream) {
+  if (batch != 0 && !out) {
+    // Let the shared checks report other errors first.
+    Sizes s;
+    const int rc = check_paged(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                               num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                               num_blocks, max_seq_len, partition_tokens, workspace,
+                               workspace_bytes, dtype, &s);
+    return rc ? rc : KVD_ERR_NULL;
+  }
+  int rc = decode_attn_paged_append_partials(q, k_cache, v_cache, k_new, v_new, block_table,
+                                             seq_lens, batch, num_q_heads, num_kv_heads,
+                                             head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                             max_seq_len, scale, partition_tokens, workspace,
+                                             workspace_bytes, dtype, stream);
+  if (rc || batch == 0) return rc;
+  return decode_attn_merge(out, seq_lens, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                           partition_tokens, workspace, workspace_bytes, dtype, stream);
 }
 
 static int mla_setup(const void* q, const void* c_cache, const int32_t* block_table,

@@ -110,17 +110,19 @@ __device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b
 // after the block's nvalid valid tokens: rows past them (the unused tail of a
 // sequence's last block, contents arbitrary) and a block with nvalid == 0
 // read back as zeros without touching memory.
+// Token rows tok (grp + 8 tok) of KV head g from K and V arrays laid out like
+// a cache block (token rows of num_kv_heads * head_dim values), nvalid rows.
 template <bool BF16, int D>
-__device__ __forceinline__ void load_block(Frag<BF16, D>& f, const PagedLaunch& a, int lane, int g,
-                                           int blk, int nvalid) {
+__device__ __forceinline__ void load_rows(Frag<BF16, D>& f, const uint32_t* kbase,
+                                          const uint32_t* vbase, const PagedLaunch& a, int lane,
+                                          int g, int nvalid) {
   using S = RowShape<BF16, D>;
   const int grp = lane >> 3;
   const int sub = lane & 7;
   const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * S::RW;  // words per token
-  const size_t base = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens * tok_stride;
   const int bytes = nvalid * static_cast<int>(tok_stride) * 4;
-  const BufRsrc rk = make_rsrc(static_cast<const uint32_t*>(a.k_cache) + base, bytes);
-  const BufRsrc rv = make_rsrc(static_cast<const uint32_t*>(a.v_cache) + base, bytes);
+  const BufRsrc rk = make_rsrc(kbase, bytes);
+  const BufRsrc rv = make_rsrc(vbase, bytes);
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok) {
     const uint32_t off = static_cast<uint32_t>(
@@ -131,6 +133,16 @@ __device__ __forceinline__ void load_block(Frag<BF16, D>& f, const PagedLaunch& 
       buffer_load_words<S::CW>(&f.v[tok][c * S::CW], rv, off + c * 8 * S::CW * 4);
     }
   }
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ void load_block(Frag<BF16, D>& f, const PagedLaunch& a, int lane, int g,
+                                           int blk, int nvalid) {
+  using S = RowShape<BF16, D>;
+  const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * S::RW;
+  const size_t base = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens * tok_stride;
+  load_rows<BF16, D>(f, static_cast<const uint32_t*>(a.k_cache) + base,
+                     static_cast<const uint32_t*>(a.v_cache) + base, a, lane, g, nvalid);
 }
 
 // One block through the online softmax of HPW heads; nvalid tokens count.
@@ -257,13 +269,21 @@ __device__ __forceinline__ void merge_groups(HeadState<HPW, DPL>& st) {
 // query heads h0 .. h0 + HPW - 1, which all read KV head g; tokens at or past
 // t_end carry no weight.  Block ids are read 64 at a time, one per lane, and
 // broadcast with readlane.  On return the lane groups are merged.
+// With `fused` (the range ends at the sequence's last position t_end - 1 and
+// this step's K/V rows are given): that position is taken from k_new / v_new
+// instead of the cache, as the last token of the softmax, and when
+// `write_new` the wave also stores KV head g's part of the rows into their
+// cache slot (the append of the same step).
 template <bool BF16, int D, int HPW, int NBUF, bool PBF16>
 __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, int g, int h0,
                                        int j_begin, int j_end, int t_end,
-                                       HeadState<HPW, D / 8>& st) {
+                                       HeadState<HPW, D / 8>& st, bool fused = false,
+                                       bool write_new = false) {
   uint32_t qv[HPW][RowShape<BF16, D>::W];
   load_query<BF16, D, HPW>(a, lane, b, h0, qv);
   reset_state(st);
+  const int t_last = t_end - 1;  // the appended position when fused
+  if (fused) t_end = t_last;
   const float sl2 = a.scale * kLog2e;
   const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
   Frag<BF16, D> buf[NBUF];
@@ -299,6 +319,31 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
         int nv;
         const int blk = block_of(jj + NBUF, nv);
         load_block<BF16, D>(buf[s0], a, lane, g, blk, nv);
+      }
+    }
+  }
+  if (fused) {
+    // The new rows, as token slot 0 of lane group 0 of a one-token block.
+    using S = RowShape<BF16, D>;
+    const int blk = wave_uniform(trow[t_last / kBlockTokens]);
+    if (blk >= 0 && blk < a.num_blocks) {
+      const size_t row_words = static_cast<size_t>(a.num_kv_heads) * S::RW;
+      const size_t src = static_cast<size_t>(b) * row_words;
+      Frag<BF16, D> f;
+      load_rows<BF16, D>(f, static_cast<const uint32_t*>(a.k_new) + src,
+                         static_cast<const uint32_t*>(a.v_new) + src, a, lane, g, 1);
+      softmax_block<BF16, D, HPW, PBF16>(f, qv, lane, 1, sl2, st);
+      if (write_new && lane < 8) {
+        const size_t dst = (static_cast<size_t>(blk) * kBlockTokens + t_last % kBlockTokens) * row_words +
+                           g * S::RW;
+        // The fused entry point receives writable caches.
+        uint32_t* kd = static_cast<uint32_t*>(const_cast<void*>(a.k_cache)) + dst;
+        uint32_t* vd = static_cast<uint32_t*>(const_cast<void*>(a.v_cache)) + dst;
+#pragma unroll
+        for (int c = 0; c < S::NCH; ++c) {
+          store_words<S::CW>(kd + S::chunk_word(c, lane), &f.k[0][c * S::CW]);
+          store_words<S::CW>(vd + S::chunk_word(c, lane), &f.v[0][c * S::CW]);
+        }
       }
     }
   }
@@ -394,7 +439,8 @@ void paged_partials_kernel(PagedLaunch a) {
   const int h0 = g * ratio + hc * HPW;
 
   HeadState<HPW, D / 8> st;
-  attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + nblk, t_end, st);
+  const bool fused = a.k_new != nullptr && t_end == len;
+  attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + nblk, t_end, st, fused, hc == 0);
   const size_t P = a.num_partitions;
   write_partial<BF16, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P, st);
 }
@@ -495,7 +541,9 @@ void paged_balanced_kernel(PagedLaunch a) {
       const int g = u / hchunks, hc = u % hchunks;
       const int h0 = g * ratio + hc * HPW;
       const int t_end = wave_uniform(min(a.seq_lens[b], a.max_seq_len));
-      attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st);
+      const bool fused = a.k_new != nullptr && seg_end == seg_begin + nb;
+      attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st,
+                                        fused, hc == 0);
       const int first = owner(seg_begin);
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;

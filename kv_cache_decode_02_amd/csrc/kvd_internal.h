@@ -41,6 +41,10 @@ struct PagedLaunch {
   float scale;
   bool bf16;
   int* counts;  // balanced split: piece counts per (b, h); NULL for fixed partitions
+  // Fused append: this step's K/V rows [B, H_kv, D] (both NULL otherwise);
+  // k_cache / v_cache are then written (the new rows' slots only).
+  const void* k_new;
+  const void* v_new;
 };
 
 struct MergeLaunch {

@@ -155,3 +155,24 @@ def test_mla_rejections():
     need = kvd.decode_attn_workspace_bytes(2, 128, 1, 512, 4096, 0)
     assert mla(wsb=need - 1) == EWS
     assert mla(B=0, q=None, o=None, ws=None, wsb=0) == OK
+
+
+def fused(**kw):
+    a = dict(o=P, q=P, k=P, v=P, kn=P, vn=P, bt=P, sl=P, B=2, hq=32, hkv=8, d=128, bs=16, mb=64,
+             nb=128, L=1024, scale=0.088, pt=0, ws=P, wsb=1 << 40, dt=1)
+    a.update(kw)
+    return lib.decode_attn_paged_append(a["o"], a["q"], a["k"], a["v"], a["kn"], a["vn"], a["bt"],
+                                        a["sl"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                        a["mb"], a["nb"], a["L"], a["scale"], a["pt"], a["ws"],
+                                        a["wsb"], a["dt"], None)
+
+
+def test_fused_append_rejections():
+    assert fused(kn=None) == ENULL
+    assert fused(vn=None) == ENULL
+    assert fused(o=None) == ENULL
+    assert fused(q=None) == ENULL
+    assert fused(kn=ctypes.c_void_p(0x1008)) == ESHAPE   # k_new not 16-byte aligned
+    assert fused(hq=24) == EUNSUP
+    assert fused(ws=None) == EWS
+    assert fused(B=0, o=None, kn=None, vn=None, ws=None, wsb=0) == OK

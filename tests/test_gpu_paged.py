@@ -113,6 +113,29 @@ def test_decode_parity(name, c):
     log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")
 
 
+@pytest.mark.parametrize("name,c", DECODE_CASES, ids=[n for n, _ in DECODE_CASES])
+def test_fused_append_parity(name, c):
+    # decode_attn_paged_append = kv_append_paged + decode_attn_paged in one pass: the
+    # caches afterwards equal the oracle's append bit for bit, the output meets the
+    # contract against the oracle (the new slot holds the NaN sentinel before the
+    # call, so reading it instead of k_new / v_new would show).
+    log(f"fused append {name}")
+    inp = make_paged_decode(np.random.default_rng(zlib.crc32(name.encode()) + 1), c["B"],
+                            c["H_q"], c["H_kv"], c["d"], c["lens"], dtype=c.get("dtype", "bf16"),
+                            table=c.get("table", "permuted"))
+    dev = Paged(inp)
+    out = kvd.decode_attn_paged_append(dev.q, dev.k_cache, dev.v_cache, dev.k_new, dev.v_new,
+                                       dev.table, dev.seq, inp.max_seq_len,
+                                       partition_tokens=c["pt"])
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.append_paged(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new,
+                                       inp.block_table, inp.seq_lens)
+    assert np.array_equal(down_bits(dev.k_cache).view(np.uint8), k_ref.view(np.uint8))
+    assert np.array_equal(down_bits(dev.v_cache).view(np.uint8), v_ref.view(np.uint8))
+    rep = assert_contract(down_f64(out), _oracle_out(inp), name)
+    log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")
+
+
 def test_tiny_config_both_layers():
     for layer, inp in enumerate(make_config_inputs("tiny")):
         log(f"tiny layer {layer}")

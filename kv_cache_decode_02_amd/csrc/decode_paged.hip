@@ -41,9 +41,10 @@ constexpr int kMaxPartitionBlocks = 64;  // one block id per lane
 constexpr int kMinPieceBlocks = kBalancedMinPieceBlocks;
 // Relative share of a workgroup on an even and an odd XCD (workgroup k runs
 // on XCD k mod 8).  Measured on MI355X with the GQA decode batch: streaming
-// the same number of blocks takes the odd XCDs about 6% longer, on every
-// repetition and on different boards, so the even ones get 6% more.
-constexpr long long kEvenXcdShare = 1059;
+// the same number of blocks takes the odd XCDs 6-9% longer, on every
+// repetition and on different boards; a sweep of the even share over 1.00 ..
+// 1.17 gives the shortest kernel at 1.11 - 1.14.
+constexpr long long kEvenXcdShare = 1120;
 constexpr long long kOddXcdShare = 1000;
 
 template <bool BF16, int D>

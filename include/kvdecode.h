@@ -100,7 +100,7 @@ int kv_append_paged(void* k_cache, void* v_cache, const void* k_new, const void*
  * positive (it must then be a multiple of 16), otherwise the library's
  * automatic choice.  For the paged path the automatic choice is 0, the
  * balanced split (below); for the latent path (head_dim = d_c = 512) and for
- * batches above 16383 it is a partition size.  Returns a negative status for
+ * batches above 8191 it is a partition size.  Returns a negative status for
  * invalid sizes.
  */
 int decode_attn_partition_tokens(int batch, int num_q_heads, int num_kv_heads, int head_dim,

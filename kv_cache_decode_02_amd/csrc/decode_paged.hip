@@ -46,6 +46,9 @@ constexpr int kMinPieceBlocks = kBalancedMinPieceBlocks;
 // 1.17 gives the shortest kernel at 1.11 - 1.14.
 constexpr long long kEvenXcdShare = 1120;
 constexpr long long kOddXcdShare = 1000;
+// Virtual blocks charged for each segment (sequence, unit group) a share
+// starts: the restart of the load pipeline costs about one block's time.
+constexpr int kSegmentCost = 1;
 
 template <bool BF16, int D>
 struct RowShape {
@@ -465,7 +468,10 @@ void paged_partials_kernel(PagedLaunch a) {
 template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_balanced_kernel(PagedLaunch a) {
-  extern __shared__ int blk_prefix[];  // [batch + 1]: blocks of the sequences before b
+  // [batch + 1] blocks of the sequences before b, then [batch + 1] count of
+  // the non-empty sequences before b.
+  extern __shared__ int blk_prefix[];
+  int* const seq_prefix = blk_prefix + a.batch + 1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int ratio = a.num_q_heads / a.num_kv_heads;
@@ -474,58 +480,92 @@ void paged_balanced_kernel(PagedLaunch a) {
   const int n_ug = (units + WG - 1) / WG;
 
   if (wave == 0) {
-    int run = 0;
+    int run = 0, run_seq = 0;
     for (int c = 0; c < a.batch; c += kWave) {
       int x = c + lane < a.batch ? seq_blocks(a, c + lane) : 0;
+      int y = x > 0 ? 1 : 0;
 #pragma unroll
       for (int sh = 1; sh < kWave; sh <<= 1) {
-        const int y = __shfl_up(x, sh, kWave);
-        if (lane >= sh) x += y;
+        const int xs = __shfl_up(x, sh, kWave);
+        const int ys = __shfl_up(y, sh, kWave);
+        if (lane >= sh) {
+          x += xs;
+          y += ys;
+        }
       }
-      if (c + lane < a.batch) blk_prefix[c + lane + 1] = run + x;
+      if (c + lane < a.batch) {
+        blk_prefix[c + lane + 1] = run + x;
+        seq_prefix[c + lane + 1] = run_seq + y;
+      }
       run += __shfl(x, kWave - 1, kWave);
+      run_seq += __shfl(y, kWave - 1, kWave);
     }
-    if (lane == 0) blk_prefix[0] = 0;
+    if (lane == 0) {
+      blk_prefix[0] = 0;
+      seq_prefix[0] = 0;
+    }
   }
   __syncthreads();
 
   // Prefix reads are wave-uniform; readfirstlane tells the compiler, which
   // would otherwise keep the segment state in VGPRs under masked branches.
   auto prefix = [&](int i) __attribute__((always_inline)) { return wave_uniform(blk_prefix[i]); };
+  // Shares are cut in a virtual list where every segment (b, ug) is preceded
+  // by kSegmentCost items of no work: a share that starts a new segment pays
+  // for the restart of its load pipeline with fewer blocks.
+  auto vprefix = [&](int i) __attribute__((always_inline)) {
+    return n_ug * (prefix(i) + kSegmentCost * wave_uniform(seq_prefix[i]));
+  };
   const int total = n_ug * prefix(a.batch);
+  const int vtotal = vprefix(a.batch);
   const int groups = gridDim.x;
   const int wg = blockIdx.x;
-  const bool weighted = total >= groups * (kMinPieceBlocks + 1);
-  const int per = max(kMinPieceBlocks, (total + groups - 1) / groups);  // equal shares
+  const bool weighted = vtotal >= groups * 2 * kMinPieceBlocks;
+  const int per = max(kMinPieceBlocks, (vtotal + groups - 1) / groups);  // equal shares
   // Weight of the first k workgroups (even ones: indices 0, 2, 4, ...).
   auto weight = [&](int k) __attribute__((always_inline)) {
     return kEvenXcdShare * ((k + 1) / 2) + kOddXcdShare * (k / 2);
   };
   const long long wsum = weight(groups);
   auto bound = [&](int k) __attribute__((always_inline)) {
-    return weighted ? static_cast<int>(static_cast<long long>(total) * weight(k) / wsum)
-                    : min(total, k * per);
+    return weighted ? static_cast<int>(static_cast<long long>(vtotal) * weight(k) / wsum)
+                    : min(vtotal, k * per);
   };
-  // Workgroup whose share holds item x.
-  auto owner = [&](int x) __attribute__((always_inline)) {
-    if (!weighted) return x / per;
-    int k = static_cast<int>(static_cast<long long>(x) * groups / total);
-    while (k + 1 < groups && bound(k + 1) <= x) ++k;
-    while (k > 0 && bound(k) > x) --k;
+  // Workgroup whose share holds virtual position v.
+  auto owner = [&](int v) __attribute__((always_inline)) {
+    if (!weighted) return v / per;
+    int k = static_cast<int>(static_cast<long long>(v) * groups / vtotal);
+    while (k + 1 < groups && bound(k + 1) <= v) ++k;
+    while (k > 0 && bound(k) > v) --k;
     return k;
   };
-  int item = bound(wg);
-  const int end = bound(wg + 1);
+  // Virtual position of block j of segment (b, ug), nb blocks per segment.
+  auto vpos = [&](int b_, int ug, int nb, int j) __attribute__((always_inline)) {
+    return vprefix(b_) + ug * (nb + kSegmentCost) + kSegmentCost + j;
+  };
+  // The first real item at or after virtual position v, and its sequence (the
+  // last b whose virtual items start at or before v, never an empty one).
+  auto to_real = [&](int v, int& b_out) __attribute__((always_inline)) {
+    if (v >= vtotal) {
+      b_out = a.batch;
+      return total;
+    }
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (vprefix(mid) <= v) lo = mid; else hi = mid - 1;
+    }
+    const int nb = prefix(lo + 1) - prefix(lo);
+    const int off = v - vprefix(lo);
+    const int ug = off / (nb + kSegmentCost);
+    const int j = max(0, off - ug * (nb + kSegmentCost) - kSegmentCost);
+    b_out = lo;
+    return n_ug * prefix(lo) + ug * nb + j;
+  };
+  int b, b_end;
+  int item = to_real(bound(wg), b);
+  const int end = to_real(bound(wg + 1), b_end);
   if (item >= end) return;  // whole workgroup
-
-  // Sequence of the first item: the last b whose items start at or before it
-  // (never an empty sequence, whose start equals its successor's).
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (n_ug * prefix(mid) <= item) lo = mid; else hi = mid - 1;
-  }
-  int b = lo;
 
   const size_t P = a.num_partitions;
   HeadState<HPW, D / 8> st;
@@ -545,11 +585,12 @@ void paged_balanced_kernel(PagedLaunch a) {
       const bool fused = a.k_new != nullptr && seg_end == seg_begin + nb;
       attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st,
                                         fused, hc == 0);
-      const int first = owner(seg_begin);
+      const int first = owner(vpos(b, ug, nb, 0));
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
       write_partial<BF16, D, HPW>(a, lane, row0 * P + piece, P, st);
-      if (piece == 0 && lane < HPW) a.counts[row0 + lane] = owner(seg_begin + nb - 1) - first + 1;
+      if (piece == 0 && lane < HPW)
+        a.counts[row0 + lane] = owner(vpos(b, ug, nb, nb - 1)) - first + 1;
     }
     item = seg_end;
     if (item == base + n_ug * nb) {
@@ -588,7 +629,7 @@ hipError_t launch_variant(const PagedLaunch& a, hipStream_t stream) {
 // wavefronts per compute unit, in workgroups of WG waves).
 template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = BF16>
 hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(a.batch + 1) * sizeof(int);
+  const size_t lds = 2 * static_cast<size_t>(a.batch + 1) * sizeof(int);
   const int groups = device_cus() * ((4 * WPE) / WG);
   hipLaunchKernelGGL((paged_balanced_kernel<BF16, D, HPW, NBUF, WPE, WG, PBF16>),
                      dim3(static_cast<unsigned>(groups)), dim3(64 * WG), lds, stream, a);

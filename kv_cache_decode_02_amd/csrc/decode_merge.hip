@@ -15,6 +15,26 @@
 namespace kvd {
 namespace {
 
+// out[b][h] = acc / den, rounded to the output type (a sequence without
+// positions has den = 0 and gets zeros).
+template <bool BF16, int D>
+__device__ __forceinline__ void write_out(const MergeLaunch& a, int bh, int lane, bool active,
+                                          const float (&acc)[D >= kWave ? D / kWave : 1],
+                                          float den) {
+  constexpr int DL = D >= kWave ? D / kWave : 1;
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  if (!active) return;
+  if constexpr (BF16) {
+    uint16_t* out = static_cast<uint16_t*>(a.out) + bh * D + lane * DL;
+#pragma unroll
+    for (int d = 0; d < DL; ++d) out[d] = to_bf16_bits(acc[d] * inv);
+  } else {
+    float* out = static_cast<float*>(a.out) + bh * D + lane * DL;
+#pragma unroll
+    for (int d = 0; d < DL; ++d) out[d] = acc[d] * inv;
+  }
+}
+
 // WPB wavefronts per (b, h): one (four (b, h) per 256-thread workgroup) when
 // a (b, h) has few pieces, four (one (b, h) per workgroup) when it may have
 // many; the waves of one (b, h) take every WPB-th run of 64 slots and add
@@ -40,6 +60,37 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + bh * P;
   const float* o = a.ws_o + bh * P * D;
 
+  const bool active = lane * DL < D;
+  // Few pieces (the usual case of the balanced split): one round trip for
+  // the (m, l) pairs and the rows together.
+  if (WPB == 1 && np <= kRows) {
+    const float2 v = lane < np ? ml[lane] : make_float2(kMinusBig, 0.f);
+    float rows[kRows][DL];
+#pragma unroll
+    for (int k = 0; k < kRows; ++k)
+#pragma unroll
+      for (int d = 0; d < DL; ++d)
+        rows[k][d] = (k < np && active) ? o[k * D + lane * DL + d] : 0.f;
+    float M = v.y > 0.f ? v.x : kMinusBig;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
+    const float w_lane = v.y > 0.f ? exp2_fast(v.x - M) : 0.f;
+    float den = w_lane * v.y;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) den += shfl_xor_f(den, s);
+    float acc[DL];
+#pragma unroll
+    for (int d = 0; d < DL; ++d) acc[d] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const float w = __shfl(w_lane, k, kWave);
+#pragma unroll
+      for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);
+    }
+    write_out<BF16, D>(a, bh, lane, active, acc, den);
+    return;
+  }
+
   // Pass 1, lanes over slots: the common maximum.  Slots with l = 0 (pieces
   // without valid tokens) carry no weight and are skipped.
   float M = kMinusBig;
@@ -59,7 +110,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
 
   // Pass 2: runs of 64 slots; the non-empty ones from a ballot, their weights
   // from the owning lane, their rows kRows at a time.
-  const bool active = lane * DL < D;
   float acc[DL];
 #pragma unroll
   for (int d = 0; d < DL; ++d) acc[d] = 0.f;
@@ -114,18 +164,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
 #pragma unroll
     for (int w = 1; w < WPB; ++w) den += red[w][D + 1];
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
-  if (active) {
-    if constexpr (BF16) {
-      uint16_t* out = static_cast<uint16_t*>(a.out) + bh * D + lane * DL;
-#pragma unroll
-      for (int d = 0; d < DL; ++d) out[d] = to_bf16_bits(acc[d] * inv);
-    } else {
-      float* out = static_cast<float*>(a.out) + bh * D + lane * DL;
-#pragma unroll
-      for (int d = 0; d < DL; ++d) out[d] = acc[d] * inv;
-    }
-  }
+  write_out<BF16, D>(a, bh, lane, active, acc, den);
 }
 
 template <bool BF16, int WPB>

@@ -1,39 +1,13 @@
-// Log-sum-exp merge of split-KV partials into the decode output.
-//
-// For one (b, h) the partitions p = 0 .. P_b - 1 carry (m_p, l_p, acc_p) with
-// m_p in log2 units, l_p = sum 2^(z' - m_p) and acc_p = sum 2^(z' - m_p) V.
-// With M = max_p m_p the softmax over all positions is
-//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,
-// the exact regrouping of the stable softmax of "KV缓存原理与显存估算"
-// (知识点二: subtracting one common maximum leaves the softmax unchanged).
-// A sequence with no positions gets zeros.  Fixed partitions: P_b =
-// ceil(L_b / partition); balanced split: P_b is the piece count that the
-// partial kernel recorded.
+// Log-sum-exp merge of split-KV partials into the decode output (the
+// combination itself is in kvd_merge.h).  A sequence with no positions gets
+// zeros.  Fixed partitions: P_b = ceil(L_b / partition); balanced split: P_b
+// is the piece count that the partial kernel recorded.
 #include "kvd_device.h"
 #include "kvd_internal.h"
+#include "kvd_merge.h"
 
 namespace kvd {
 namespace {
-
-// out[b][h] = acc / den, rounded to the output type (a sequence without
-// positions has den = 0 and gets zeros).
-template <bool BF16, int D>
-__device__ __forceinline__ void write_out(const MergeLaunch& a, int bh, int lane, bool active,
-                                          const float (&acc)[D >= kWave ? D / kWave : 1],
-                                          float den) {
-  constexpr int DL = D >= kWave ? D / kWave : 1;
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
-  if (!active) return;
-  if constexpr (BF16) {
-    uint16_t* out = static_cast<uint16_t*>(a.out) + bh * D + lane * DL;
-#pragma unroll
-    for (int d = 0; d < DL; ++d) out[d] = to_bf16_bits(acc[d] * inv);
-  } else {
-    float* out = static_cast<float*>(a.out) + bh * D + lane * DL;
-#pragma unroll
-    for (int d = 0; d < DL; ++d) out[d] = acc[d] * inv;
-  }
-}
 
 // WPB wavefronts per (b, h): one (four (b, h) per 256-thread workgroup) when
 // a (b, h) has few pieces, four (one (b, h) per workgroup) when it may have
@@ -42,8 +16,7 @@ __device__ __forceinline__ void write_out(const MergeLaunch& a, int bh, int lane
 // time.
 template <bool BF16, int D, int WPB>
 __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
-  constexpr int DL = D >= kWave ? D / kWave : 1;  // dims per lane
-  constexpr int kRows = 8;
+  constexpr int DL = MergeShape<D>::DL, kRows = MergeShape<D>::kRows;
   __shared__ float red[WPB][D + 2];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -61,33 +34,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
   const float* o = a.ws_o + bh * P * D;
 
   const bool active = lane * DL < D;
-  // Few pieces (the usual case of the balanced split): one round trip for
-  // the (m, l) pairs and the rows together.
-  if (WPB == 1 && np <= kRows) {
-    const float2 v = lane < np ? ml[lane] : make_float2(kMinusBig, 0.f);
-    float rows[kRows][DL];
-#pragma unroll
-    for (int k = 0; k < kRows; ++k)
-#pragma unroll
-      for (int d = 0; d < DL; ++d)
-        rows[k][d] = (k < np && active) ? o[k * D + lane * DL + d] : 0.f;
-    float M = v.y > 0.f ? v.x : kMinusBig;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
-    const float w_lane = v.y > 0.f ? exp2_fast(v.x - M) : 0.f;
-    float den = w_lane * v.y;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) den += shfl_xor_f(den, s);
-    float acc[DL];
-#pragma unroll
-    for (int d = 0; d < DL; ++d) acc[d] = 0.f;
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const float w = __shfl(w_lane, k, kWave);
-#pragma unroll
-      for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);
-    }
-    write_out<BF16, D>(a, bh, lane, active, acc, den);
+  if constexpr (WPB == 1) {
+    float acc[DL], den;
+    merge_pieces<D>(ml, o, np, lane, acc, den);
+    store_merged<BF16, D>(a.out, bh, lane, acc, den);
     return;
   }
 
@@ -164,7 +114,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
 #pragma unroll
     for (int w = 1; w < WPB; ++w) den += red[w][D + 1];
   }
-  write_out<BF16, D>(a, bh, lane, active, acc, den);
+  store_merged<BF16, D>(a.out, bh, lane, acc, den);
 }
 
 template <bool BF16, int WPB>

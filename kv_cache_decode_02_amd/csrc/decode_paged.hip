@@ -354,29 +354,41 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
   merge_groups(st);
 }
 
-// After merge_groups every lane group holds all heads; lane group h (< HPW)
-// writes query head h0 + h to workspace slot slot0 + h * stride (slot =
-// (b * H_q + head) * P + piece).  The group's values are picked with selects,
-// so all stores sit under one branch.
-template <bool BF16, int D, int HPW>
-__device__ __forceinline__ void write_partial(const PagedLaunch& a, int lane, size_t slot0,
-                                              size_t stride, const HeadState<HPW, D / 8>& st) {
-  using S = RowShape<BF16, D>;
-  constexpr int DPL = S::DPL;
+// After merge_groups every lane group holds all heads: lane group h (< HPW)
+// takes head h.  The values are picked with selects (an indexed access into
+// the state would put it in scratch memory).
+template <int DPL>
+struct GroupRow {
+  float m, l, v[DPL];
+};
+
+template <int HPW, int DPL>
+__device__ __forceinline__ GroupRow<DPL> pick_group(const HeadState<HPW, DPL>& st, int lane) {
   const int grp = lane >> 3;
-  const int sub = lane & 7;
-  float vals[DPL];
-  float mv = st.m[0], lv = st.l[0];
+  GroupRow<DPL> r;
+  r.m = st.m[0];
+  r.l = st.l[0];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) vals[e] = st.acc[0][e];
+  for (int e = 0; e < DPL; ++e) r.v[e] = st.acc[0][e];
 #pragma unroll
   for (int h = 1; h < HPW; ++h) {
     const bool mine = grp == h;
-    mv = mine ? st.m[h] : mv;
-    lv = mine ? st.l[h] : lv;
+    r.m = mine ? st.m[h] : r.m;
+    r.l = mine ? st.l[h] : r.l;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) vals[e] = mine ? st.acc[h][e] : vals[e];
+    for (int e = 0; e < DPL; ++e) r.v[e] = mine ? st.acc[h][e] : r.v[e];
   }
+  return r;
+}
+
+// Lane group h (< HPW) writes its row to workspace slot slot0 + h * stride
+// (slot = (b * H_q + head) * P + piece); all stores sit under one branch.
+template <bool BF16, int D, int HPW>
+__device__ __forceinline__ void write_partial(const PagedLaunch& a, int lane, size_t slot0,
+                                              size_t stride, const GroupRow<D / 8>& r) {
+  using S = RowShape<BF16, D>;
+  const int grp = lane >> 3;
+  const int sub = lane & 7;
   if (grp < HPW) {
     const size_t slot = slot0 + grp * stride;
     float* orow = a.ws_o + slot * D;
@@ -388,15 +400,10 @@ __device__ __forceinline__ void write_partial(const PagedLaunch& a, int lane, si
     for (int c = 0; c < S::NCH; ++c)
 #pragma unroll
       for (int v = 0; v < RUN / 4; ++v) {
-        const float* x = &vals[c * RUN + 4 * v];
+        const float* x = &r.v[c * RUN + 4 * v];
         *reinterpret_cast<float4*>(orow + (c * 8 + sub) * RUN + 4 * v) = make_float4(x[0], x[1], x[2], x[3]);
       }
-    if (sub == 0) {
-      float2 ml;
-      ml.x = mv;
-      ml.y = lv;
-      reinterpret_cast<float2*>(a.ws_ml)[slot] = ml;
-    }
+    if (sub == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * slot) = make_float2(r.m, r.l);
   }
 }
 
@@ -446,7 +453,8 @@ void paged_partials_kernel(PagedLaunch a) {
   const bool fused = a.k_new != nullptr && t_end == len;
   attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + nblk, t_end, st, fused, hc == 0);
   const size_t P = a.num_partitions;
-  write_partial<BF16, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P, st);
+  write_partial<BF16, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P,
+                              pick_group(st, lane));
 }
 
 // Balanced split (automatic mode).  The work list is every (sequence b,
@@ -588,7 +596,7 @@ void paged_balanced_kernel(PagedLaunch a) {
       const int first = owner(vpos(b, ug, nb, 0));
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
-      write_partial<BF16, D, HPW>(a, lane, row0 * P + piece, P, st);
+      write_partial<BF16, D, HPW>(a, lane, row0 * P + piece, P, pick_group(st, lane));
       if (piece == 0 && lane < HPW)
         a.counts[row0 + lane] = owner(vpos(b, ug, nb, nb - 1)) - first + 1;
     }

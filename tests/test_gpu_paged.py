@@ -160,6 +160,64 @@ def test_phases_equal_single_call():
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
+SPLIT_CASES = [
+    ("gqa-r4", dict(B=5, H_q=32, H_kv=8, d=128, lens=[4096, 40, 17, 1000, 300], dtype="bf16")),
+    ("mha-d64", dict(B=3, H_q=16, H_kv=16, d=64, lens=[2000, 33, 700], dtype="bf16")),
+    ("r2-f32", dict(B=3, H_q=8, H_kv=4, d=128, lens=[1500, 16, 2], dtype="f32")),
+    ("r8-two-chunks", dict(B=2, H_q=64, H_kv=8, d=128, lens=[3000, 100], dtype="bf16")),
+]
+
+
+@pytest.mark.parametrize("name,c", SPLIT_CASES, ids=[n for n, _ in SPLIT_CASES])
+def test_balanced_split_with_an_empty_sequence(name, c):
+    # Balanced split (automatic mode) with sequence 1 at length 0 between
+    # sequences cut into many pieces: the empty one gets zeros, the others
+    # meet the contract, and the one-call path equals partials + merge.
+    log(f"balanced split {name}")
+    inp = make_paged_decode(np.random.default_rng(zlib.crc32(name.encode()) + 2), c["B"],
+                            c["H_q"], c["H_kv"], c["d"], c["lens"], dtype=c["dtype"])
+    dev = Paged(inp)
+    kvd.kv_append_paged(dev.k_cache, dev.v_cache, dev.k_new, dev.v_new, dev.table, dev.seq)
+    seq = dev.seq.clone()
+    seq[1] = 0
+    L = inp.max_seq_len
+    one = kvd.decode_attn_paged(dev.q, dev.k_cache, dev.v_cache, dev.table, seq, L)
+    ws = kvd.alloc_workspace(inp.B, c["H_q"], c["H_kv"], c["d"], L)
+    kvd.decode_attn_paged_partials(dev.q, dev.k_cache, dev.v_cache, dev.table, seq, L, ws)
+    two = torch.empty_like(dev.q)
+    kvd.decode_attn_merge(two, seq, c["H_kv"], L, ws)
+    torch.cuda.synchronize()
+    iv = torch.int16 if c["dtype"] == "bf16" else torch.int32
+    assert torch.equal(one.view(iv), two.view(iv))
+    assert torch.count_nonzero(one[1]).item() == 0
+    keep = [b for b in range(inp.B) if b != 1]  # the others do not see sequence 1
+    assert_contract(down_f64(one)[keep], _oracle_out(inp)[keep], name)
+
+
+def test_workspace_serves_calls_of_any_size():
+    # One workspace, sized for the largest call and never cleared, used by
+    # calls of different batch, heads and lengths in turn (the data of one
+    # call lands where the next keeps other data): each output equals that of
+    # a fresh workspace.
+    log("workspace reuse")
+    shapes = [(6, 32, 8, 128, [4096, 1, 900, 2000, 64, 3000]), (2, 8, 2, 64, [700, 33]),
+              (3, 64, 8, 128, [1500, 4000, 16]), (6, 32, 8, 128, [100, 4096, 17, 18, 2500, 5])]
+    need = max(kvd.decode_attn_workspace_bytes(B, hq, hkv, d, max(lens), 0)
+               for B, hq, hkv, d, lens in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")  # garbage to start
+    for i, (B, hq, hkv, d, lens) in enumerate(shapes):
+        inp = make_paged_decode(np.random.default_rng(40 + i), B, hq, hkv, d, lens)
+        dev = Paged(inp)
+        kvd.kv_append_paged(dev.k_cache, dev.v_cache, dev.k_new, dev.v_new, dev.table, dev.seq)
+        got = kvd.decode_attn_paged(dev.q, dev.k_cache, dev.v_cache, dev.table, dev.seq,
+                                    inp.max_seq_len, workspace=ws)
+        fresh = kvd.decode_attn_paged(dev.q, dev.k_cache, dev.v_cache, dev.table, dev.seq,
+                                      inp.max_seq_len)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), fresh.view(torch.int16)), i
+    assert_contract(down_f64(got), _oracle_out(inp), "last reused call")
+
+
 def test_block_placement_is_bit_identical():
     log("placement")
     a = make_paged_decode(np.random.default_rng(8), 3, 32, 8, 128, [700, 33, 1600])

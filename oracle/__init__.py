@@ -20,6 +20,7 @@ Modules:
   attention  single-query decode attention, split partials + LSE merge,
              absorbed MLA, full causal recompute
   capacity   KV byte accounting (per token, useful / padded / paged, shared)
+  quant      INT8 cache: per-channel K / per-token V codes, append, decode
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against values
 printed on the pages (``tests/golden/``), closed forms, invariants and special
@@ -39,6 +40,16 @@ from .attention import (
     mla_decode_paged,
     causal_attention,
 )
+from .quant import (
+    quantize,
+    token_scale,
+    channel_scales,
+    append_paged_int8,
+    dequantize_k,
+    dequantize_v,
+    decode_attn_paged_int8,
+    history_int8,
+)
 from .capacity import (
     bytes_per_token,
     paged_capacity,
@@ -55,4 +66,6 @@ __all__ = [
     "mla_decode", "mla_decode_paged", "causal_attention",
     "bytes_per_token", "paged_capacity", "unique_block_bytes",
     "kv_cache_bytes", "mla_elements_per_token",
+    "quantize", "token_scale", "channel_scales", "append_paged_int8", "dequantize_k",
+    "dequantize_v", "decode_attn_paged_int8", "history_int8",
 ]

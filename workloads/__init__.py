@@ -12,6 +12,8 @@ from .gen import (
     MlaInputs,
     bf16_round_bits,
     make_paged_decode,
+    PagedInt8Inputs,
+    make_paged_decode_int8,
     make_mla,
     BLOCK_SIZE,
     UNUSED_TABLE_ENTRY,
@@ -20,6 +22,7 @@ from .configs import CONFIGS, config, make_config_inputs
 
 __all__ = [
     "PagedDecodeInputs", "MlaInputs", "bf16_round_bits", "make_paged_decode",
+    "PagedInt8Inputs", "make_paged_decode_int8",
     "make_mla", "BLOCK_SIZE", "UNUSED_TABLE_ENTRY", "CONFIGS", "config",
     "make_config_inputs",
 ]

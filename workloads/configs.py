@@ -13,6 +13,10 @@
   mla_deepseek_v2 absorbed MLA, 128 query heads, latent 512 + RoPE key 64
                   (576 bf16 per token), batch 32, every length 4096, q and
                   latent N(0, (1/24)^2), output in latent space (512)
+  gqa_llama3_8b_int8
+                  the gqa_llama3_8b batch (same seed, so the same lengths)
+                  over an INT8 cache: per-channel K and per-token V scales,
+                  bf16 queries and output
 
 Seeds: config k (1..5 in the order above) uses numpy default_rng(42 + k); 42
 is the seed of the pages' own numpy sketch.  Lengths are drawn first, then the
@@ -21,7 +25,7 @@ generator's fixed draw order (``workloads.gen``).
 
 import numpy as np
 
-from .gen import make_paged_decode, make_mla
+from .gen import make_paged_decode, make_paged_decode_int8, make_mla
 
 CONFIGS = {
     "tiny": dict(index=1, kind="paged", B=1, H_q=4, H_kv=4, d=32, layers=2,
@@ -39,6 +43,9 @@ CONFIGS = {
     "mla_deepseek_v2": dict(index=5, kind="mla", B=32, H=128, d_c=512, d_rope=64, layers=1,
                             lens=("fixed", 4096), dtype="bf16", table="permuted",
                             std=1.0 / 24.0, partition=0),
+    "gqa_llama3_8b_int8": dict(index=3, kind="paged_int8", B=64, H_q=32, H_kv=8, d=128,
+                               layers=1, lens=("uniform", 512, 8192), dtype="int8",
+                               table="permuted", std=1.0, partition=0),
 }
 
 
@@ -77,6 +84,10 @@ def make_config_inputs(name, sentinel="nan", rng=None):
             layers.append(make_paged_decode(rng, B, cfg["H_q"], cfg["H_kv"], cfg["d"], lens,
                                             dtype=cfg["dtype"], table=cfg["table"],
                                             std=cfg["std"], sentinel=sentinel))
+        elif cfg["kind"] == "paged_int8":
+            layers.append(make_paged_decode_int8(rng, B, cfg["H_q"], cfg["H_kv"], cfg["d"], lens,
+                                                 table=cfg["table"], std=cfg["std"],
+                                                 sentinel=sentinel))
         else:
             layers.append(make_mla(rng, B, cfg["H"], cfg["d_c"], cfg["d_rope"], lens,
                                    std=cfg["std"], table=cfg["table"], sentinel=sentinel))

@@ -24,6 +24,15 @@ NaN output) or zero in timing runs.
 
 Draw order from the generator (fixed): block permutation, q, K pool, V pool,
 k_new, v_new.  Sequence lengths are drawn by the caller before this.
+
+INT8 caches (``make_paged_decode_int8``) hold codes in [-127, 127] drawn
+uniformly, per-channel K scales [H_kv, d] and per-token V scales
+[NB, block_size, H_kv] drawn uniformly in std * [0.5, 1.5] / 64, so that the
+cached values have roughly the spread of the bf16 workloads; k_new / v_new are
+bf16 draws (the append quantises them).  Unfilled slots hold code -128 (never
+written by the append) and a NaN V scale in parity runs, code 0 and scale 0
+in timing runs.  Draw order: block permutation, q, K codes, V codes, V
+scales, K scales, k_new, v_new.
 """
 
 from dataclasses import dataclass
@@ -218,3 +227,81 @@ def make_mla(rng, B, H, d_c, d_rope, seq_lens, std, table="permuted", sentinel="
         _mark_unfilled(c_pool, owned, lens, block_size, _sentinel("bf16", sentinel))
     return MlaInputs(B, H, d_c, d_rope, block_size, lens.astype(np.int32), bt, nb,
                      q, c_pool, c_new)
+
+
+def _codes(rng, shape):
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.int8)
+    for start in range(0, n, _CHUNK):
+        stop = min(start + _CHUNK, n)
+        out[start:stop] = rng.integers(-127, 128, size=stop - start, dtype=np.int8)
+    return out.reshape(shape)
+
+
+def _scales(rng, shape, std):
+    v = rng.random(int(np.prod(shape)), dtype=np.float32) + np.float32(0.5)
+    return (v * np.float32(std / 64.0)).reshape(shape)
+
+
+@dataclass
+class PagedInt8Inputs:
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    block_size: int
+    seq_lens: np.ndarray
+    block_table: np.ndarray
+    num_blocks: int
+    q: np.ndarray        # bf16 bits [B, H_q, d]
+    kq_pool: np.ndarray  # int8 [NB, 16, H_kv, d]
+    vq_pool: np.ndarray  # int8 [NB, 16, H_kv, d]
+    vs_pool: np.ndarray  # fp32 [NB, 16, H_kv]
+    k_scale: np.ndarray  # fp32 [H_kv, d]
+    k_new: np.ndarray    # bf16 bits [B, H_kv, d]
+    v_new: np.ndarray    # bf16 bits [B, H_kv, d]
+    dtype: str = "bf16"  # of q, k_new, v_new and the output
+
+    @property
+    def max_blocks_per_seq(self):
+        return int(self.block_table.shape[1])
+
+    @property
+    def max_seq_len(self):
+        return int(self.seq_lens.max())
+
+    @property
+    def kv_bytes_read(self):
+        """Codes of K and V plus the V scales of all visible positions."""
+        n = int(self.seq_lens.astype(np.int64).sum())
+        return int(n * self.H_kv * (2 * self.d + 4))
+
+
+def make_paged_decode_int8(rng, B, H_q, H_kv, d, seq_lens, table="permuted", std=1.0,
+                           sentinel="nan", max_blocks_per_seq=None, block_size=BLOCK_SIZE):
+    """Draw one decode step's inputs over an INT8 cache (see the module docstring)."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if lens.shape != (B,) or np.any(lens < 1):
+        raise ValueError("seq_lens must have B entries, each >= 1")
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    mb = max_blocks_per_seq or _blocks_needed(lens.max(), block_size)
+    bt, nb, owned = _assign_blocks(rng, lens, block_size, mb, table)
+    q = _draw(rng, (B, H_q, d), std, "bf16")
+    kq = _codes(rng, (nb, block_size, H_kv, d))
+    vq = _codes(rng, (nb, block_size, H_kv, d))
+    vs = _scales(rng, (nb, block_size, H_kv), std)
+    ks = _scales(rng, (H_kv, d), std)
+    k_new = _draw(rng, (B, H_kv, d), std, "bf16")
+    v_new = _draw(rng, (B, H_kv, d), std, "bf16")
+    if sentinel == "nan":
+        code, scale = np.int8(-128), np.float32(np.nan)
+    elif sentinel == "zero":
+        code, scale = np.int8(0), np.float32(0)
+    else:
+        raise ValueError(f"unknown sentinel {sentinel!r}")
+    _mark_unfilled(kq, owned, lens, block_size, code)
+    _mark_unfilled(vq, owned, lens, block_size, code)
+    _mark_unfilled(vs, owned, lens, block_size, scale)
+    return PagedInt8Inputs(B, H_q, H_kv, d, block_size, lens.astype(np.int32), bt, nb, q, kq, vq,
+                           vs, ks, k_new, v_new)

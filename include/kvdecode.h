@@ -263,6 +263,72 @@ int decode_attn_mla_partials(const void* q, const void* c_cache,
                              float scale, int partition_tokens, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * INT8 KV cache ("KV-Cache——为什么AI回复越来越快", KV-Cache量化: one byte per
+ * element halves the cache and the bytes a decode step reads; K is scaled per
+ * channel, every dimension of a K/V head having its own scale, and V per
+ * token, every token's row its own scale).
+ *
+ *   k_cache, v_cache [num_blocks, 16, num_kv_heads, head_dim] int8 codes in
+ *                    [-127, 127], the layout of the bf16 caches
+ *   k_scale          [num_kv_heads, head_dim] fp32, the per-channel K scales
+ *                    (a calibration chosen by the caller)
+ *   v_scale          [num_blocks, 16, num_kv_heads] fp32, one scale per token
+ *                    and K/V head, addressed like the rows
+ * A stored element stands for code * scale.
+ */
+
+/*
+ * kv_append_paged_int8 -- the append of kv_append_paged into an INT8 cache:
+ * position seq_lens[b] - 1 of sequence b gets
+ *   K codes clip(round(k_new / k_scale), -127, 127) per channel,
+ *   V scale s = max |v_new row| / 127 (per K/V head) and V codes
+ *   clip(round(v_new / s), -127, 127) (s = 0 and codes 0 for a zero row),
+ * every step in fp32 with correctly rounded divisions and round-half-to-even.
+ *   k_new, v_new   [batch, num_kv_heads, head_dim] in dtype (KVD_BF16 or
+ *                  KVD_F32), finite
+ *   head_dim       32, 64 or 128
+ * Other arguments, preconditions and errors as for kv_append_paged.
+ */
+int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const void* k_new,
+                         const void* v_new, const float* k_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int num_blocks,
+                         kvd_dtype_t dtype, void* stream);
+
+/*
+ * decode_attn_paged_int8 -- decode_attn_paged over an INT8 cache: the same
+ * attention with K[t][g][j] = k_scale[g][j] * code and V[t][g][j] =
+ * v_scale[t][g] * code.  The scales are folded into the query (per channel)
+ * and into the softmax weights (per token) in registers; the codes are
+ * widened to bf16 exactly and the products accumulate in fp32.
+ *   q, out     [batch, num_q_heads, head_dim] bf16 (dtype must be KVD_BF16)
+ *   k_scale    16-byte aligned; v_scale 4-byte aligned
+ * Other arguments (head_dim, ratios, partition_tokens, workspace), errors and
+ * preconditions as for decode_attn_paged; the workspace is sized by
+ * decode_attn_workspace_bytes with the same arguments.
+ */
+int decode_attn_paged_int8(void* out, const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* seq_lens, int batch,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                           int partition_tokens, void* workspace, size_t workspace_bytes,
+                           kvd_dtype_t dtype, void* stream);
+
+/*
+ * decode_attn_paged_int8_partials -- first phase of decode_attn_paged_int8
+ * only (same arguments minus `out`); finish with decode_attn_merge.
+ */
+int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int max_blocks_per_seq, int num_blocks,
+                                    int max_seq_len, float scale, int partition_tokens,
+                                    void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

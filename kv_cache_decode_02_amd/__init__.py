@@ -3,8 +3,10 @@
 One decode step of one layer: ``kv_append_paged`` writes the step's K/V row
 into the paged cache, ``decode_attn_paged`` attends over the whole visible
 history (split-KV partials, then a log-sum-exp merge), and
-``decode_attn_paged_append`` does both in one pass; ``decode_attn_mla`` is
-the absorbed multi-head latent attention variant over a latent cache.  The functions mirror
+``decode_attn_paged_append`` does both in one pass; ``kv_append_paged_int8``
+and ``decode_attn_paged_int8`` are the same step over an INT8 cache (K scaled
+per channel, V per token); ``decode_attn_mla`` is the absorbed multi-head
+latent attention variant over a latent cache.  The functions mirror
 the C ABI in ``include/kvdecode.h`` and only marshal arguments; importing this
 package fails if the HIP library has not been built.
 """
@@ -23,6 +25,9 @@ from ._native import (
     decode_attn_mla,
     decode_attn_mla_partials,
     mla_default_scale,
+    kv_append_paged_int8,
+    decode_attn_paged_int8,
+    decode_attn_paged_int8_partials,
     LIB_PATH,
     HEADER_PATH,
 )
@@ -32,5 +37,6 @@ __all__ = [
     "decode_attn_paged_append", "decode_attn_paged_append_partials",
     "decode_attn_merge", "decode_attn_workspace_bytes", "decode_attn_partition_tokens",
     "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials", "mla_default_scale",
+    "kv_append_paged_int8", "decode_attn_paged_int8", "decode_attn_paged_int8_partials",
     "LIB_PATH", "HEADER_PATH",
 ]

@@ -56,6 +56,14 @@ lib.decode_attn_mla.restype = _i
 lib.decode_attn_mla.argtypes = [_vp] + _MLA_ARGS
 lib.decode_attn_mla_partials.restype = _i
 lib.decode_attn_mla_partials.argtypes = _MLA_ARGS
+lib.kv_append_paged_int8.restype = _i
+lib.kv_append_paged_int8.argtypes = [_vp] * 8 + [_i] * 7 + [_vp]
+# q, k_cache, v_cache, k_scale, v_scale, then the paged arguments from block_table on
+_INT8_ARGS = _PAGED_ARGS[:3] + [_vp, _vp] + _PAGED_ARGS[3:]
+lib.decode_attn_paged_int8.restype = _i
+lib.decode_attn_paged_int8.argtypes = [_vp] + _INT8_ARGS
+lib.decode_attn_paged_int8_partials.restype = _i
+lib.decode_attn_paged_int8_partials.argtypes = _INT8_ARGS
 lib.decode_attn_merge.restype = _i
 lib.decode_attn_merge.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]
 
@@ -295,3 +303,93 @@ def decode_attn_mla_partials(q, c_cache, block_table, seq_lens, max_seq_len, wor
     args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
                      partition_tokens, workspace)
     _check(lib.decode_attn_mla_partials(*args, _stream(stream)), "decode_attn_mla_partials")
+
+
+# --- INT8 cache -----------------------------------------------------------------
+
+def kv_append_paged_int8(k_cache, v_cache, v_scale, k_new, v_new, k_scale, block_table,
+                         seq_lens, stream=None):
+    """Quantise each sequence's new row into position seq_lens[b] - 1 of an INT8
+    cache: K per channel with ``k_scale`` [H_kv, d], V per token (the scale of
+    the row goes to ``v_scale`` [num_blocks, 16, H_kv]).
+
+    k_cache/v_cache: int8 [num_blocks, 16, H_kv, d]; k_new/v_new: [B, H_kv, d]
+    bf16 or fp32.
+    """
+    _need(k_cache, "k_cache", dtype=torch.int8)
+    _need(v_cache, "v_cache", dtype=torch.int8)
+    _need(v_scale, "v_scale", dtype=torch.float32)
+    _need(k_scale, "k_scale", dtype=torch.float32)
+    _need(k_new, "k_new")
+    _need(v_new, "v_new", dtype=k_new.dtype)
+    _need(block_table, "block_table", dtype=torch.int32)
+    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    nb, bs, h_kv, d = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(v_scale.shape) != (nb, bs, h_kv):
+        raise KvdError("v_cache must match k_cache and v_scale be [num_blocks, 16, H_kv]")
+    if tuple(k_scale.shape) != (h_kv, d):
+        raise KvdError("k_scale must be [H_kv, d]")
+    B = k_new.shape[0]
+    if tuple(k_new.shape) != (B, h_kv, d) or tuple(v_new.shape) != (B, h_kv, d):
+        raise KvdError("k_new and v_new must be [B, H_kv, d]")
+    status = lib.kv_append_paged_int8(_ptr(k_cache), _ptr(v_cache), _ptr(v_scale), _ptr(k_new),
+                                      _ptr(v_new), _ptr(k_scale), _ptr(block_table),
+                                      _ptr(seq_lens), B, h_kv, d, bs, block_table.shape[1], nb,
+                                      _dtype_code(k_new), _stream(stream))
+    _check(status, "kv_append_paged_int8")
+
+
+def _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len, scale,
+               partition_tokens, ws):
+    for t, n in ((q, "q"), (block_table, "block_table"), (seq_lens, "seq_lens"),
+                 (ws, "workspace")):
+        _need(t, n)
+    _need(q, "q", dtype=torch.bfloat16)
+    _need(k_cache, "k_cache", dtype=torch.int8)
+    _need(v_cache, "v_cache", dtype=torch.int8)
+    _need(k_scale, "k_scale", dtype=torch.float32)
+    _need(v_scale, "v_scale", dtype=torch.float32)
+    _need(block_table, "block_table", dtype=torch.int32)
+    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    B, h_q, d = q.shape
+    nb, bs, h_kv, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise KvdError("q, k_cache and v_cache head sizes disagree")
+    if tuple(k_scale.shape) != (h_kv, d) or tuple(v_scale.shape) != (nb, bs, h_kv):
+        raise KvdError("k_scale must be [H_kv, d] and v_scale [num_blocks, 16, H_kv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_table), _ptr(seq_lens), B, h_q, h_kv, d, bs, block_table.shape[1], nb,
+            int(max_seq_len), float(scale), int(partition_tokens), _ptr(ws),
+            ws.numel() * ws.element_size(), KVD_BF16]
+
+
+def decode_attn_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
+                           max_seq_len, scale=None, partition_tokens=0, workspace=None, out=None,
+                           stream=None):
+    """Decode attention of bf16 q [B, H_q, d] over an INT8 paged cache; returns
+    the bf16 output."""
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    if workspace is None:
+        workspace = alloc_workspace(B, h_q, h_kv, d, max_seq_len, partition_tokens,
+                                    device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=torch.bfloat16)
+    args = _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                      scale, partition_tokens, workspace)
+    _check(lib.decode_attn_paged_int8(_ptr(out), *args, _stream(stream)),
+           "decode_attn_paged_int8")
+    return out
+
+
+def decode_attn_paged_int8_partials(q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                    seq_lens, max_seq_len, workspace, scale=None,
+                                    partition_tokens=0, stream=None):
+    """First phase of decode_attn_paged_int8 only; finish with decode_attn_merge."""
+    args = _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                      scale, partition_tokens, workspace)
+    _check(lib.decode_attn_paged_int8_partials(*args, _stream(stream)),
+           "decode_attn_paged_int8_partials")

@@ -241,6 +241,9 @@ static PagedLaunch paged_launch(const void* q, const void* k_cache, const void* 
                  : nullptr;
   a.k_new = nullptr;
   a.v_new = nullptr;
+  a.int8 = false;
+  a.k_scale = nullptr;
+  a.v_scale = nullptr;
   return a;
 }
 
@@ -374,6 +377,106 @@ int decode_attn_paged_append(void* out, const void* q, void* k_cache, void* v_ca
   if (rc || batch == 0) return rc;
   return decode_attn_merge(out, seq_lens, batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                            partition_tokens, workspace, workspace_bytes, dtype, stream);
+}
+
+int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const void* k_new,
+                         const void* v_new, const float* k_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int num_blocks,
+                         kvd_dtype_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return KVD_ERR_UNSUPPORTED;
+  if (batch < 0 || num_kv_heads < 1) return KVD_ERR_SHAPE;
+  if (!(head_dim == 32 || head_dim == 64 || head_dim == 128)) return KVD_ERR_UNSUPPORTED;
+  if (block_size != kBlockSize) return KVD_ERR_UNSUPPORTED;
+  if (max_blocks_per_seq < 1 || max_blocks_per_seq > kMaxTableBlocks || num_blocks < 1)
+    return KVD_ERR_SHAPE;
+  if (batch == 0) return KVD_OK;
+  if (!k_cache || !v_cache || !v_scale || !k_new || !v_new || !k_scale || !block_table ||
+      !seq_lens)
+    return KVD_ERR_NULL;
+  AppendInt8Launch a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.v_scale = v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_scale = k_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.bf16 = dtype == KVD_BF16;
+  return hip_status(launch_append_int8(a, static_cast<hipStream_t>(stream)));
+}
+
+// The INT8 decode takes bf16 queries (and writes a bf16 output); its scales
+// are fp32, the per-channel K scales read 16 bytes at a time.
+static int check_paged_int8(const void* q, const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table, const int32_t* seq_lens, int batch,
+                            int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                            int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                            int partition_tokens, const void* workspace, size_t workspace_bytes,
+                            int dtype, Sizes* s) {
+  if (dtype != KVD_BF16) return KVD_ERR_UNSUPPORTED;
+  const int rc = check_paged(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                             num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                             max_seq_len, partition_tokens, workspace, workspace_bytes, dtype, s);
+  if (rc || batch == 0) return rc;
+  if (!k_scale || !v_scale) return KVD_ERR_NULL;
+  if (!aligned16(k_scale) || (reinterpret_cast<uintptr_t>(v_scale) & 3u) != 0) return KVD_ERR_SHAPE;
+  return KVD_OK;
+}
+
+int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int max_blocks_per_seq, int num_blocks,
+                                    int max_seq_len, float scale, int partition_tokens,
+                                    void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                                    void* stream) {
+  Sizes s;
+  const int rc = check_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
+                                  batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_blocks_per_seq, num_blocks, max_seq_len, partition_tokens,
+                                  workspace, workspace_bytes, dtype, &s);
+  if (rc || batch == 0) return rc;
+  PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                               num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
+                               max_seq_len, scale, workspace, dtype, s);
+  a.int8 = true;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return hip_status(launch_paged_partials(a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_paged_int8(void* out, const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table, const int32_t* seq_lens, int batch,
+                           int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                           int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                           int partition_tokens, void* workspace, size_t workspace_bytes,
+                           kvd_dtype_t dtype, void* stream) {
+  Sizes s;
+  int rc = check_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
+                            num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            num_blocks, max_seq_len, partition_tokens, workspace,
+                            workspace_bytes, dtype, &s);
+  if (rc || batch == 0) return rc;
+  if (!out) return KVD_ERR_NULL;
+  rc = decode_attn_paged_int8_partials(q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                       seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                       block_size, max_blocks_per_seq, num_blocks, max_seq_len,
+                                       scale, partition_tokens, workspace, workspace_bytes,
+                                       dtype, stream);
+  if (rc) return rc;
+  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
+                                     workspace, dtype, s);
+  return hip_status(launch_merge(m, static_cast<hipStream_t>(stream)));
 }
 
 static int mla_setup(const void* q, const void* c_cache, const int32_t* block_table,

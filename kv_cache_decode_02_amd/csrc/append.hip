@@ -38,7 +38,82 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
   }
 }
 
+// INT8 cache ("KV-Cache——为什么AI回复越来越快", KV-Cache量化: K per channel, V
+// per token): code = clip(round_half_even(x / s), -127, 127), every step in
+// fp32 with correctly rounded divisions; K takes the caller's per-channel
+// scales, V the scale max |v| / 127 of its own row (0 and all codes 0 for a
+// zero row), stored beside the codes.  One wave per (sequence, KV head);
+// lane l handles dimensions l, l + 64, ...
+__device__ __forceinline__ int8_t quantize_code(float x, float s) {
+  if (!(s > 0.f)) return 0;
+  const float r = rintf(__fdiv_rn(x, s));
+  return static_cast<int8_t>(fminf(fmaxf(r, -127.f), 127.f));
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void append_int8_kernel(AppendInt8Launch a) {
+  constexpr int EPL = (D + kWave - 1) / kWave;  // elements per lane
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int len = a.seq_lens[b];
+  const long long cap = static_cast<long long>(a.max_blocks_per_seq) * kBlockTokens;
+  if (len < 1 || len > cap) return;  // violated precondition: write nothing
+  const int pos = len - 1;
+  const int blk = a.block_table[static_cast<size_t>(b) * a.max_blocks_per_seq + pos / kBlockTokens];
+  if (blk < 0 || blk >= a.num_blocks) return;
+  const size_t row = static_cast<size_t>(blk) * kBlockTokens + pos % kBlockTokens;
+
+  for (int g = threadIdx.x >> 6; g < a.num_kv_heads; g += blockDim.x >> 6) {
+    const size_t src = (static_cast<size_t>(b) * a.num_kv_heads + g) * D;
+    const size_t dst = (row * a.num_kv_heads + g) * D;
+    float kx[EPL], vx[EPL];
+    float vmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int j = lane + i * kWave;
+      kx[i] = vx[i] = 0.f;
+      if (j < D) {
+        if constexpr (BF16) {
+          kx[i] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.k_new)[src + j]) << 16);
+          vx[i] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.v_new)[src + j]) << 16);
+        } else {
+          kx[i] = static_cast<const float*>(a.k_new)[src + j];
+          vx[i] = static_cast<const float*>(a.v_new)[src + j];
+        }
+        vmax = fmaxf(vmax, fabsf(vx[i]));
+      }
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) vmax = fmaxf(vmax, shfl_xor_f(vmax, sh));
+    const float vs = __fdiv_rn(vmax, 127.f);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int j = lane + i * kWave;
+      if (j < D) {
+        a.k_cache[dst + j] = quantize_code(kx[i], a.k_scale[static_cast<size_t>(g) * D + j]);
+        a.v_cache[dst + j] = quantize_code(vx[i], vs);
+      }
+    }
+    if (lane == 0) a.v_scale[row * a.num_kv_heads + g] = vs;
+  }
+}
+
+template <bool BF16>
+hipError_t launch_append_int8_typed(const AppendInt8Launch& a, hipStream_t stream) {
+  const dim3 grid(a.batch), block(256);
+  switch (a.head_dim) {
+    case 32: hipLaunchKernelGGL((append_int8_kernel<BF16, 32>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((append_int8_kernel<BF16, 64>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((append_int8_kernel<BF16, 128>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream) {
+  return a.bf16 ? launch_append_int8_typed<true>(a, stream) : launch_append_int8_typed<false>(a, stream);
+}
 
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream) {
   dim3 grid(a.batch, a.v_cache ? 2 : 1);

@@ -36,6 +36,10 @@
 namespace kvd {
 namespace {
 
+// Storage of the K/V cache: fp32, bf16, or INT8 codes with per-channel K and
+// per-token V scales.
+enum Kind : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+
 constexpr float kRaise = 8.0f;
 constexpr int kMaxPartitionBlocks = 64;  // one block id per lane
 constexpr int kMinPieceBlocks = kBalancedMinPieceBlocks;
@@ -50,14 +54,17 @@ constexpr long long kOddXcdShare = 1000;
 // starts: the restart of the load pipeline costs about one block's time.
 constexpr int kSegmentCost = 1;
 
-template <bool BF16, int D>
+template <int KT, int D>
 struct RowShape {
-  static constexpr int EPW = BF16 ? 2 : 1;  // elements per 32-bit word
+  static constexpr int EPW = KT == kF32 ? 1 : (KT == kBF16 ? 2 : 4);  // elements per word
   static constexpr int DPL = D / 8;         // elements of a row per lane
   static constexpr int W = DPL / EPW;       // words of a row per lane
   static constexpr int CW = W < 4 ? W : 4;  // words per vector load
   static constexpr int NCH = W / CW;        // vector loads per row per lane
   static constexpr int RW = D / EPW;        // words per row (one head)
+  // Query words per lane: INT8 codes are widened to bf16 pairs, so each code
+  // word meets two words of (scaled) query.
+  static constexpr int QW = KT == kI8 ? 2 * W : W;
   static_assert(W >= 1 && W % CW == 0, "unsupported head_dim");
   // Word offset, inside a row, of the lane's chunk c.
   static __device__ __forceinline__ int chunk_word(int c, int sub) { return (c * 8 + sub) * CW; }
@@ -86,27 +93,53 @@ __device__ __forceinline__ void reset_state(HeadState<HPW, DPL>& st) {
   }
 }
 
-// The K and V rows of the lane's two token slots of one block.
-template <bool BF16, int D>
+// The K and V rows of the lane's two token slots of one block (INT8: codes,
+// and the two tokens' V scales).
+template <int KT, int D>
 struct Frag {
-  uint32_t k[2][RowShape<BF16, D>::W];
-  uint32_t v[2][RowShape<BF16, D>::W];
+  uint32_t k[2][RowShape<KT, D>::W];
+  uint32_t v[2][RowShape<KT, D>::W];
+  float vs[KT == kI8 ? 2 : 1];
 };
 
 // Query slice of heads h0 .. h0 + HPW - 1 of sequence b, in the lane layout of
-// the K rows.
-template <bool BF16, int D, int HPW>
-__device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b, int h0,
-                                           uint32_t (&qv)[HPW][RowShape<BF16, D>::W]) {
-  using S = RowShape<BF16, D>;
+// the K rows.  INT8 cache: the query is bf16 and is multiplied by KV head g's
+// per-channel K scales (q . (s * code) = (q * s) . code), then rounded to
+// fp16 pairs that meet the widened codes in dot2 (fp16 keeps 11 bits of the
+// scaled query; bf16's 8 would cost ~0.5% in the scores).
+template <int KT, int D, int HPW>
+__device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b, int h0, int g,
+                                           uint32_t (&qv)[HPW][RowShape<KT, D>::QW]) {
+  using S = RowShape<KT, D>;
   const int sub = lane & 7;
-  const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
-                       (static_cast<size_t>(b) * a.num_q_heads + h0) * S::RW;
-#pragma unroll
-  for (int h = 0; h < HPW; ++h)
+  if constexpr (KT == kI8) {
+    const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
+                         (static_cast<size_t>(b) * a.num_q_heads + h0) * (D / 2);
+    const float* ks = a.k_scale + static_cast<size_t>(g) * D;
 #pragma unroll
     for (int c = 0; c < S::NCH; ++c)
-      load_words<S::CW>(&qv[h][c * S::CW], qw + h * S::RW + S::chunk_word(c, sub));
+#pragma unroll
+      for (int w = 0; w < S::CW; ++w) {
+        const int d0 = (S::chunk_word(c, sub) + w) * 4;  // the code word's 4 dimensions
+        const float4 s4 = *reinterpret_cast<const float4*>(ks + d0);
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+          uint32_t q2[2];
+          load_words<2>(q2, qw + h * (D / 2) + d0 / 2);
+          const int k = c * S::CW + w;
+          qv[h][2 * k] = pack_f16x2(bf16_lo(q2[0]) * s4.x, bf16_hi(q2[0]) * s4.y);
+          qv[h][2 * k + 1] = pack_f16x2(bf16_lo(q2[1]) * s4.z, bf16_hi(q2[1]) * s4.w);
+        }
+      }
+  } else {
+    const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
+                         (static_cast<size_t>(b) * a.num_q_heads + h0) * S::RW;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h)
+#pragma unroll
+      for (int c = 0; c < S::NCH; ++c)
+        load_words<S::CW>(&qv[h][c * S::CW], qw + h * S::RW + S::chunk_word(c, sub));
+  }
 }
 
 // Issues the loads of physical block `blk` for KV head g: the lane's two token
@@ -116,11 +149,11 @@ __device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b
 // read back as zeros without touching memory.
 // Token rows tok (grp + 8 tok) of KV head g from K and V arrays laid out like
 // a cache block (token rows of num_kv_heads * head_dim values), nvalid rows.
-template <bool BF16, int D>
-__device__ __forceinline__ void load_rows(Frag<BF16, D>& f, const uint32_t* kbase,
+template <int KT, int D>
+__device__ __forceinline__ void load_rows(Frag<KT, D>& f, const uint32_t* kbase,
                                           const uint32_t* vbase, const PagedLaunch& a, int lane,
-                                          int g, int nvalid) {
-  using S = RowShape<BF16, D>;
+                                          int g, int nvalid, const float* sbase = nullptr) {
+  using S = RowShape<KT, D>;
   const int grp = lane >> 3;
   const int sub = lane & 7;
   const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * S::RW;  // words per token
@@ -137,41 +170,76 @@ __device__ __forceinline__ void load_rows(Frag<BF16, D>& f, const uint32_t* kbas
       buffer_load_words<S::CW>(&f.v[tok][c * S::CW], rv, off + c * 8 * S::CW * 4);
     }
   }
+  if constexpr (KT == kI8) {
+    // V scales [token][KV head] of the block, nvalid tokens.
+    const BufRsrc rs = make_rsrc(sbase, nvalid * a.num_kv_heads * 4);
+#pragma unroll
+    for (int tok = 0; tok < 2; ++tok)
+      f.vs[tok] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rs, static_cast<uint32_t>(((grp + 8 * tok) * a.num_kv_heads + g) * 4), 0, 0));
+  }
 }
 
-template <bool BF16, int D>
-__device__ __forceinline__ void load_block(Frag<BF16, D>& f, const PagedLaunch& a, int lane, int g,
+template <int KT, int D>
+__device__ __forceinline__ void load_block(Frag<KT, D>& f, const PagedLaunch& a, int lane, int g,
                                            int blk, int nvalid) {
-  using S = RowShape<BF16, D>;
+  using S = RowShape<KT, D>;
   const size_t tok_stride = static_cast<size_t>(a.num_kv_heads) * S::RW;
-  const size_t base = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens * tok_stride;
-  load_rows<BF16, D>(f, static_cast<const uint32_t*>(a.k_cache) + base,
-                     static_cast<const uint32_t*>(a.v_cache) + base, a, lane, g, nvalid);
+  const size_t blk0 = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens;
+  const size_t base = blk0 * tok_stride;
+  load_rows<KT, D>(f, static_cast<const uint32_t*>(a.k_cache) + base,
+                   static_cast<const uint32_t*>(a.v_cache) + base, a, lane, g, nvalid,
+                   KT == kI8 ? a.v_scale + blk0 * a.num_kv_heads : nullptr);
 }
 
 // One block through the online softmax of HPW heads; nvalid tokens count.
-template <bool BF16, int D, int HPW, bool PBF16>
-__device__ __forceinline__ void softmax_block(const Frag<BF16, D>& f,
-                                              const uint32_t (&qv)[HPW][RowShape<BF16, D>::W],
+template <int KT, int D, int HPW, bool PBF16>
+__device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
+                                              const uint32_t (&qv)[HPW][RowShape<KT, D>::QW],
                                               int lane, int nvalid, float sl2,
                                               HeadState<HPW, D / 8>& st) {
-  static_assert(BF16 || !PBF16, "bf16 weights need a bf16 cache");
-  using S = RowShape<BF16, D>;
+  static_assert(KT != kF32 || !PBF16, "bf16 weights need a 16- or 8-bit cache");
+  using S = RowShape<KT, D>;
   constexpr int W = S::W, DPL = S::DPL;
   const int grp = lane >> 3;
   float (&m)[HPW] = st.m;
   float (&l)[HPW] = st.l;
   float (&acc)[HPW][DPL] = st.acc;
   float s[2][HPW];
+  // INT8: the codes widened to fp16 (exact), once for all heads: K as pairs
+  // of neighbouring dimensions, V as (token 0, token 1) pairs of one
+  // dimension.
+  uint32_t kp[KT == kI8 ? 2 : 1][KT == kI8 ? 2 * W : 1];
+  uint32_t vp[KT == kI8 ? DPL : 1];
+  if constexpr (KT == kI8) {
+    auto code = [](uint32_t word, int i) __attribute__((always_inline)) {
+      return static_cast<float>(static_cast<int8_t>(word >> (8 * i)));
+    };
+#pragma unroll
+    for (int tok = 0; tok < 2; ++tok)
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        kp[tok][2 * w] = pack_f16x2_int(code(f.k[tok][w], 0), code(f.k[tok][w], 1));
+        kp[tok][2 * w + 1] = pack_f16x2_int(code(f.k[tok][w], 2), code(f.k[tok][w], 3));
+      }
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vp[4 * w + i] = pack_f16x2_int(code(f.v[0][w], i), code(f.v[1][w], i));
+  }
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok) {
     const bool ok = grp + 8 * tok < nvalid;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
       float part = 0.f;
+      if constexpr (KT == kI8) {
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        if constexpr (BF16) {
+        for (int i = 0; i < 2 * W; ++i) part = dot2_f16(qv[h][i], kp[tok][i], part);
+      }
+#pragma unroll
+      for (int w = 0; w < (KT == kI8 ? 0 : W); ++w) {
+        if constexpr (KT == kBF16) {
           part = dot2_bf16(qv[h][w], f.k[tok][w], part);
         } else {
           part = fmaf(__uint_as_float(qv[h][w]), __uint_as_float(f.k[tok][w]), part);
@@ -186,7 +254,7 @@ __device__ __forceinline__ void softmax_block(const Frag<BF16, D>& f,
   // For bf16 weights: the V elements of the lane's two tokens, paired per
   // dimension (shared by all heads of the group).
   uint32_t vlo[PBF16 ? W : 1], vhi[PBF16 ? W : 1];
-  if constexpr (PBF16) {
+  if constexpr (KT == kBF16) {
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       vlo[w] = pair_lo(vw[0][w], vw[1][w]);
@@ -207,7 +275,15 @@ __device__ __forceinline__ void softmax_block(const Frag<BF16, D>& f,
     }
     const float p0 = exp2_fast(s[0][h] - m[h]);
     const float p1 = exp2_fast(s[1][h] - m[h]);
-    if constexpr (PBF16) {
+    if constexpr (KT == kI8) {
+      // INT8: the weights times the tokens' V scales meet the widened codes
+      // (p * (s * code) = (p * s) * code) as fp16 pairs; the sum takes the
+      // plain weights, rounded the same way.
+      l[h] = dot2_f16(pack_f16x2(p0, p1), kF16OnePair, l[h]);
+      const uint32_t pp = pack_f16x2(p0 * f.vs[0], p1 * f.vs[1]);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = dot2_f16(pp, vp[e], acc[h][e]);
+    } else if constexpr (PBF16) {
       // Weights rounded to bf16 and paired over the lane's two tokens; the
       // same rounded weights feed the sum, so the output stays an exact
       // convex combination of V rows.  Products accumulate in fp32.
@@ -222,7 +298,7 @@ __device__ __forceinline__ void softmax_block(const Frag<BF16, D>& f,
       l[h] += p0 + p1;
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        if constexpr (BF16) {
+        if constexpr (KT == kBF16) {
           acc[h][2 * w] = fmaf(p1, bf16_lo(vw[1][w]), fmaf(p0, bf16_lo(vw[0][w]), acc[h][2 * w]));
           acc[h][2 * w + 1] =
               fmaf(p1, bf16_hi(vw[1][w]), fmaf(p0, bf16_hi(vw[0][w]), acc[h][2 * w + 1]));
@@ -278,19 +354,19 @@ __device__ __forceinline__ void merge_groups(HeadState<HPW, DPL>& st) {
 // instead of the cache, as the last token of the softmax, and when
 // `write_new` the wave also stores KV head g's part of the rows into their
 // cache slot (the append of the same step).
-template <bool BF16, int D, int HPW, int NBUF, bool PBF16>
+template <int KT, int D, int HPW, int NBUF, bool PBF16>
 __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, int g, int h0,
                                        int j_begin, int j_end, int t_end,
                                        HeadState<HPW, D / 8>& st, bool fused = false,
                                        bool write_new = false) {
-  uint32_t qv[HPW][RowShape<BF16, D>::W];
-  load_query<BF16, D, HPW>(a, lane, b, h0, qv);
+  uint32_t qv[HPW][RowShape<KT, D>::QW];
+  load_query<KT, D, HPW>(a, lane, b, h0, g, qv);
   reset_state(st);
   const int t_last = t_end - 1;  // the appended position when fused
   if (fused) t_end = t_last;
   const float sl2 = a.scale * kLog2e;
   const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
-  Frag<BF16, D> buf[NBUF];
+  Frag<KT, D> buf[NBUF];
 
   for (int c0 = j_begin; c0 < j_end; c0 += kMaxPartitionBlocks) {
     const int nblk = min(kMaxPartitionBlocks, j_end - c0);
@@ -309,7 +385,7 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
     for (int s0 = 0; s0 < NBUF; ++s0) {
       int nv;
       const int blk = block_of(s0, nv);
-      load_block<BF16, D>(buf[s0], a, lane, g, blk, nv);
+      load_block<KT, D>(buf[s0], a, lane, g, blk, nv);
     }
     for (int base = 0; base < nblk; base += NBUF) {
 #pragma unroll
@@ -318,25 +394,26 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
         if (jj < nblk) {
           int nv;
           block_of(jj, nv);
-          softmax_block<BF16, D, HPW, PBF16>(buf[s0], qv, lane, nv, sl2, st);
+          softmax_block<KT, D, HPW, PBF16>(buf[s0], qv, lane, nv, sl2, st);
         }
         int nv;
         const int blk = block_of(jj + NBUF, nv);
-        load_block<BF16, D>(buf[s0], a, lane, g, blk, nv);
+        load_block<KT, D>(buf[s0], a, lane, g, blk, nv);
       }
     }
   }
-  if (fused) {
+  if (KT != kI8 && fused) {
     // The new rows, as token slot 0 of lane group 0 of a one-token block.
-    using S = RowShape<BF16, D>;
+    // (The INT8 cache has no fused append: its rows must be quantised.)
+    using S = RowShape<KT, D>;
     const int blk = wave_uniform(trow[t_last / kBlockTokens]);
     if (blk >= 0 && blk < a.num_blocks) {
       const size_t row_words = static_cast<size_t>(a.num_kv_heads) * S::RW;
       const size_t src = static_cast<size_t>(b) * row_words;
-      Frag<BF16, D> f;
-      load_rows<BF16, D>(f, static_cast<const uint32_t*>(a.k_new) + src,
+      Frag<KT, D> f;
+      load_rows<KT, D>(f, static_cast<const uint32_t*>(a.k_new) + src,
                          static_cast<const uint32_t*>(a.v_new) + src, a, lane, g, 1);
-      softmax_block<BF16, D, HPW, PBF16>(f, qv, lane, 1, sl2, st);
+      softmax_block<KT, D, HPW, PBF16>(f, qv, lane, 1, sl2, st);
       if (write_new && lane < 8) {
         const size_t dst = (static_cast<size_t>(blk) * kBlockTokens + t_last % kBlockTokens) * row_words +
                            g * S::RW;
@@ -383,10 +460,10 @@ __device__ __forceinline__ GroupRow<DPL> pick_group(const HeadState<HPW, DPL>& s
 
 // Lane group h (< HPW) writes its row to workspace slot slot0 + h * stride
 // (slot = (b * H_q + head) * P + piece); all stores sit under one branch.
-template <bool BF16, int D, int HPW>
+template <int KT, int D, int HPW>
 __device__ __forceinline__ void write_partial(const PagedLaunch& a, int lane, size_t slot0,
                                               size_t stride, const GroupRow<D / 8>& r) {
-  using S = RowShape<BF16, D>;
+  using S = RowShape<KT, D>;
   const int grp = lane >> 3;
   const int sub = lane & 7;
   if (grp < HPW) {
@@ -423,7 +500,7 @@ __device__ __forceinline__ int seq_blocks(const PagedLaunch& a, int b) {
 // KV heads (and head chunks) of one (sequence, partition), so a workgroup's
 // waves read the same blocks together: for 8 KV heads an 8-wave workgroup
 // reads whole contiguous token rows of every block.
-template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_partials_kernel(PagedLaunch a) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -451,9 +528,9 @@ void paged_partials_kernel(PagedLaunch a) {
 
   HeadState<HPW, D / 8> st;
   const bool fused = a.k_new != nullptr && t_end == len;
-  attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + nblk, t_end, st, fused, hc == 0);
+  attend<KT, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + nblk, t_end, st, fused, hc == 0);
   const size_t P = a.num_partitions;
-  write_partial<BF16, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P,
+  write_partial<KT, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P,
                               pick_group(st, lane));
 }
 
@@ -473,7 +550,7 @@ void paged_partials_kernel(PagedLaunch a) {
 // segment's first item), and the workgroup of piece 0 records the number of
 // pieces for the merge.  Pieces of one (b, h) never exceed ceil(blocks /
 // kMinPieceBlocks) + 1.
-template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_balanced_kernel(PagedLaunch a) {
   // [batch + 1] blocks of the sequences before b, then [batch + 1] count of
@@ -591,12 +668,12 @@ void paged_balanced_kernel(PagedLaunch a) {
       const int h0 = g * ratio + hc * HPW;
       const int t_end = wave_uniform(min(a.seq_lens[b], a.max_seq_len));
       const bool fused = a.k_new != nullptr && seg_end == seg_begin + nb;
-      attend<BF16, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st,
+      attend<KT, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st,
                                         fused, hc == 0);
       const int first = owner(vpos(b, ug, nb, 0));
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
-      write_partial<BF16, D, HPW>(a, lane, row0 * P + piece, P, pick_group(st, lane));
+      write_partial<KT, D, HPW>(a, lane, row0 * P + piece, P, pick_group(st, lane));
       if (piece == 0 && lane < HPW)
         a.counts[row0 + lane] = owner(vpos(b, ug, nb, nb - 1)) - first + 1;
     }
@@ -622,24 +699,24 @@ int device_cus() {
   return cus[dev];
 }
 
-template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = BF16>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = (KT != kF32)>
 hipError_t launch_variant(const PagedLaunch& a, hipStream_t stream) {
   const int ratio = a.num_q_heads / a.num_kv_heads;
   const long long units = static_cast<long long>(a.batch) * a.num_partitions * a.num_kv_heads *
                           (ratio / HPW);
   const long long blocks = (units + WG - 1) / WG;
-  hipLaunchKernelGGL((paged_partials_kernel<BF16, D, HPW, NBUF, WPE, WG, PBF16>),
+  hipLaunchKernelGGL((paged_partials_kernel<KT, D, HPW, NBUF, WPE, WG, PBF16>),
                      dim3(static_cast<unsigned>(blocks)), dim3(64 * WG), 0, stream, a);
   return hipGetLastError();
 }
 
 // Balanced split: as many workgroups as are resident at once (4 * WPE
 // wavefronts per compute unit, in workgroups of WG waves).
-template <bool BF16, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = BF16>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = (KT != kF32)>
 hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
   const size_t lds = 2 * static_cast<size_t>(a.batch + 1) * sizeof(int);
   const int groups = device_cus() * ((4 * WPE) / WG);
-  hipLaunchKernelGGL((paged_balanced_kernel<BF16, D, HPW, NBUF, WPE, WG, PBF16>),
+  hipLaunchKernelGGL((paged_balanced_kernel<KT, D, HPW, NBUF, WPE, WG, PBF16>),
                      dim3(static_cast<unsigned>(groups)), dim3(64 * WG), lds, stream, a);
   return hipGetLastError();
 }
@@ -648,41 +725,41 @@ hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
 // SIMD; four heads per wave need ~200 VGPRs (2 waves per SIMD) and do best
 // with two buffers.  Eight-wave workgroups help when a group's rows are read
 // by several wavefronts (one head per wave, or head chunks of one group).
-template <bool BF16, int D, int HPW>
+template <int KT, int D, int HPW>
 hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
-  constexpr bool kWide = BF16 || D < 128;  // register budget allows >= 2 waves
-  constexpr int NBUF = (BF16 && HPW == 1) ? 3 : 2;
+  constexpr bool kWide = KT != kF32 || D < 128;  // register budget allows >= 2 waves
+  constexpr int NBUF = (KT != kF32 && HPW == 1) ? 3 : 2;
   constexpr int WPE = (HPW == 1 && kWide) ? 3 : (kWide ? 2 : 1);
   const int ratio = a.num_q_heads / a.num_kv_heads;
   if (a.counts) {
     // Whole workgroups must fill the 4 * WPE wave slots of a compute unit.
-    if constexpr ((4 * WPE) % 8 == 0) return launch_balanced<BF16, D, HPW, NBUF, WPE, 8>(a, stream);
-    return launch_balanced<BF16, D, HPW, NBUF, WPE, 4>(a, stream);
+    if constexpr ((4 * WPE) % 8 == 0) return launch_balanced<KT, D, HPW, NBUF, WPE, 8>(a, stream);
+    return launch_balanced<KT, D, HPW, NBUF, WPE, 4>(a, stream);
   }
   if constexpr (kWide) {
-    if (HPW == 1 || ratio > HPW) return launch_variant<BF16, D, HPW, NBUF, WPE, 8>(a, stream);
+    if (HPW == 1 || ratio > HPW) return launch_variant<KT, D, HPW, NBUF, WPE, 8>(a, stream);
   }
-  return launch_variant<BF16, D, HPW, NBUF, WPE, 4>(a, stream);
+  return launch_variant<KT, D, HPW, NBUF, WPE, 4>(a, stream);
 }
 
 // Groups of more than 4 query heads are split over ratio / 4 wavefronts of the
 // same workgroup; they read the same K/V rows, the second time from cache.
-template <bool BF16, int D>
+template <int KT, int D>
 hipError_t launch_by_ratio(const PagedLaunch& a, hipStream_t stream) {
   const int ratio = a.num_q_heads / a.num_kv_heads;
   switch (ratio) {
-    case 1: return launch_typed<BF16, D, 1>(a, stream);
-    case 2: return launch_typed<BF16, D, 2>(a, stream);
-    default: return launch_typed<BF16, D, 4>(a, stream);  // multiples of 4
+    case 1: return launch_typed<KT, D, 1>(a, stream);
+    case 2: return launch_typed<KT, D, 2>(a, stream);
+    default: return launch_typed<KT, D, 4>(a, stream);  // multiples of 4
   }
 }
 
-template <bool BF16>
+template <int KT>
 hipError_t launch_by_dim(const PagedLaunch& a, hipStream_t stream) {
   switch (a.head_dim) {
-    case 32: return launch_by_ratio<BF16, 32>(a, stream);
-    case 64: return launch_by_ratio<BF16, 64>(a, stream);
-    default: return launch_by_ratio<BF16, 128>(a, stream);
+    case 32: return launch_by_ratio<KT, 32>(a, stream);
+    case 64: return launch_by_ratio<KT, 64>(a, stream);
+    default: return launch_by_ratio<KT, 128>(a, stream);
   }
 }
 
@@ -697,7 +774,8 @@ bool paged_supported(int head_dim, int ratio, bool /*bf16*/) {
 int max_partition_blocks() { return kMaxPartitionBlocks; }
 
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream) {
-  return a.bf16 ? launch_by_dim<true>(a, stream) : launch_by_dim<false>(a, stream);
+  if (a.int8) return launch_by_dim<kI8>(a, stream);
+  return a.bf16 ? launch_by_dim<kBF16>(a, stream) : launch_by_dim<kF32>(a, stream);
 }
 
 }  // namespace kvd

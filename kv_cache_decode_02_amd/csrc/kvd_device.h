@@ -46,6 +46,28 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t x, uint32_t y) {
 
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+// a.lo*b.lo + a.hi*b.hi + c with fp16 operands and fp32 accumulation.
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
+}
+
+// Two fp32 values as one fp16x2 word, round to nearest even; a to the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two integer-valued fp32 values of magnitude <= 2048 as fp16x2 (exact, so
+// the truncating conversion is as good as any).
+__device__ __forceinline__ uint32_t pack_f16x2_int(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+constexpr uint32_t kF16OnePair = 0x3C003C00u;  // (1.0, 1.0) in fp16
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int CTRL>

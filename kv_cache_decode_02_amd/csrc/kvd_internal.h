@@ -45,6 +45,12 @@ struct PagedLaunch {
   // k_cache / v_cache are then written (the new rows' slots only).
   const void* k_new;
   const void* v_new;
+  // INT8 cache: k_cache / v_cache hold codes, k_scale [H_kv, D] the
+  // per-channel K scales, v_scale [NB, 16, H_kv] the per-token V scales;
+  // q and the output are bf16.
+  bool int8;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct MergeLaunch {
@@ -71,6 +77,19 @@ struct AppendLaunch {
   bool vec16;  // all four row buffers 16-byte aligned
 };
 
+struct AppendInt8Launch {
+  int8_t* k_cache;        // [NB, 16, H_kv, D] codes
+  int8_t* v_cache;        // [NB, 16, H_kv, D] codes
+  float* v_scale;         // [NB, 16, H_kv]
+  const void* k_new;      // [B, H_kv, D] bf16 or fp32
+  const void* v_new;
+  const float* k_scale;   // [H_kv, D]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int batch, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks;
+  bool bf16;
+};
+
 struct MlaLaunch {
   const void* q;            // [B, H, d_c + d_rope] bf16
   const void* c_cache;      // [NB, 16, d_c + d_rope] bf16
@@ -85,6 +104,7 @@ struct MlaLaunch {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream);
+hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream);
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 hipError_t launch_mla_partials(const MlaLaunch& a, hipStream_t stream);

@@ -176,3 +176,47 @@ def test_fused_append_rejections():
     assert fused(hq=24) == EUNSUP
     assert fused(ws=None) == EWS
     assert fused(B=0, o=None, kn=None, vn=None, ws=None, wsb=0) == OK
+
+
+def append_int8(**kw):
+    a = dict(k=P, v=P, vs=P, kn=P, vn=P, ks=P, bt=P, sl=P, B=2, hkv=8, d=128, bs=16, mb=4, nb=8,
+             dt=1)
+    a.update(kw)
+    return lib.kv_append_paged_int8(a["k"], a["v"], a["vs"], a["kn"], a["vn"], a["ks"], a["bt"],
+                                    a["sl"], a["B"], a["hkv"], a["d"], a["bs"], a["mb"], a["nb"],
+                                    a["dt"], None)
+
+
+def test_append_int8_rejections():
+    assert append_int8(vs=None) == ENULL
+    assert append_int8(ks=None) == ENULL
+    assert append_int8(v=None) == ENULL
+    assert append_int8(d=96) == EUNSUP
+    assert append_int8(bs=32) == EUNSUP
+    assert append_int8(dt=7) == EUNSUP
+    assert append_int8(hkv=0) == ESHAPE
+    assert append_int8(mb=0) == ESHAPE
+    assert append_int8(B=0, k=None, v=None, vs=None, kn=None, vn=None, ks=None) == OK
+
+
+def paged_int8(**kw):
+    a = dict(o=P, q=P, k=P, v=P, ks=P, vs=P, bt=P, sl=P, B=2, hq=32, hkv=8, d=128, bs=16, mb=64,
+             nb=128, L=1024, scale=0.088, pt=0, ws=P, wsb=1 << 40, dt=1)
+    a.update(kw)
+    return lib.decode_attn_paged_int8(a["o"], a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"],
+                                      a["sl"], a["B"], a["hq"], a["hkv"], a["d"], a["bs"], a["mb"],
+                                      a["nb"], a["L"], a["scale"], a["pt"], a["ws"], a["wsb"],
+                                      a["dt"], None)
+
+
+def test_decode_int8_rejections():
+    assert paged_int8(dt=0) == EUNSUP                    # queries must be bf16
+    assert paged_int8(ks=None) == ENULL
+    assert paged_int8(vs=None) == ENULL
+    assert paged_int8(o=None) == ENULL
+    assert paged_int8(ks=ctypes.c_void_p(0x1004)) == ESHAPE  # k_scale not 16-byte aligned
+    assert paged_int8(vs=ctypes.c_void_p(0x1002)) == ESHAPE  # v_scale not 4-byte aligned
+    assert paged_int8(hq=24) == EUNSUP
+    assert paged_int8(d=96) == EUNSUP
+    assert paged_int8(ws=None) == EWS
+    assert paged_int8(B=0, o=None, ks=None, vs=None, ws=None, wsb=0) == OK

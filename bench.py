@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_llama3_8b",
                     choices=["gqa_llama3_8b", "mha_llama2_7b", "long_gqa_split", "tiny",
-                             "mla_deepseek_v2"])
+                             "mla_deepseek_v2", "gqa_llama3_8b_int8"])
     ap.add_argument("--replicas", type=int, default=4,
                     help="MLA: rotate over this many copies of the latent cache so the "
                          "timed reads come from HBM, not the 256 MB Infinity Cache")
@@ -211,6 +211,121 @@ def cpu_baseline_mla(inp, target_s, scale):
             "tokens_per_s": done / dt}
 
 
+def cpu_baseline_int8(inp, target_s):
+    """Time the fp64 oracle (quantising append + INT8 decode) on whole
+    sequences of the INT8 workload until ~target_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    done = tokens = 0
+    order = np.random.default_rng(0).permutation(inp.B)
+    while time.perf_counter() - t0 < target_s and done < 50 * inp.B:
+        b = int(order[done % inp.B])
+        sl = slice(b, b + 1)
+        n = int(inp.seq_lens[b])
+        # the sequence's own blocks, appended to and read as one small pool
+        blocks = inp.block_table[b, :-(-n // 16)]
+        table = np.arange(len(blocks), dtype=np.int32)[None, :]
+        kq, vq, vs = oracle.append_paged_int8(inp.kq_pool[blocks], inp.vq_pool[blocks],
+                                              inp.vs_pool[blocks], inp.k_new[sl], inp.v_new[sl],
+                                              "bf16", inp.k_scale, table, inp.seq_lens[sl])
+        oracle.decode_attn_paged_int8(inp.q[sl], kq, vq, vs, inp.k_scale, table,
+                                      inp.seq_lens[sl], "bf16")
+        done += 1
+        tokens += n
+    dt = time.perf_counter() - t0
+    return {"value": tokens * inp.H_kv * (2 * inp.d + 4) / dt / 1e9, "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} sequence decodes ({done / inp.B:.2f} passes over the {inp.B} "
+                      f"sequences, {tokens} positions, all heads) in {dt:.1f} s; fp64 numpy "
+                      f"on {os.cpu_count()} host CPUs",
+            "tokens_per_s": done / dt}
+
+
+def main_int8(args, kvd, make_config_inputs):
+    """One decode step over the INT8 cache: the quantising append, the partial
+    kernel and the merge, timed like the bf16 step (graph replay)."""
+    import torch
+    dev = torch.device("cuda:0")
+    inp = make_config_inputs(args.workload, sentinel="zero")[0]
+    pt = args.partition if args.partition >= 0 else 0
+    q = up(inp.q, dev)
+    kq, vq, vs, ks = up(inp.kq_pool, dev), up(inp.vq_pool, dev), up(inp.vs_pool, dev), up(inp.k_scale, dev)
+    kn, vn = up(inp.k_new, dev), up(inp.v_new, dev)
+    table, seq = up(inp.block_table, dev), up(inp.seq_lens, dev)
+    H_q, H_kv, d, L = inp.H_q, inp.H_kv, inp.d, inp.max_seq_len
+    pt_used = kvd.decode_attn_partition_tokens(inp.B, H_q, H_kv, d, L, pt)
+    ws = kvd.alloc_workspace(inp.B, H_q, H_kv, d, L, pt)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        kvd.kv_append_paged_int8(kq, vq, vs, kn, vn, ks, table, seq)
+        if ev is not None:
+            ev[0].record(stream)
+        kvd.decode_attn_paged_int8_partials(q, kq, vq, ks, vs, table, seq, L, ws,
+                                            partition_tokens=pt)
+        if ev is not None:
+            ev[1].record(stream)
+        kvd.decode_attn_merge(out, seq, H_kv, L, ws, partition_tokens=pt)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_eager = start.elapsed_time(end) / args.steps
+    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_avg = float(np.mean(part_ms))
+    ms_step, graph_check = ms_eager, None
+    if not args.no_graph:
+        ms_step, graph_check = time_graph(torch, step, out, args)
+    kv_bytes = inp.kv_bytes_read
+    kernel = "paged_balanced" if pt_used == 0 else "paged_partials"
+    value = kv_bytes / (ms_step / 1e3) / 1e9
+    achieved = kv_bytes / (part_avg / 1e3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "step_launch": "hip graph" if not args.no_graph else "eager",
+        "step_kernels": "kv_append_paged_int8, partials, merge",
+        "ms_per_step_eager": round(ms_eager, 5), "graph_replays_match_eager": graph_check,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": H_q,
+                   "num_kv_heads": H_kv, "head_dim": d, "block_size": 16,
+                   "sum_seq_len": int(inp.seq_lens.astype(np.int64).sum()), "max_seq_len": L,
+                   "partition_tokens": pt_used, "cache": "int8 codes, per-channel K and "
+                   "per-token V fp32 scales; bf16 queries and output"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(inp.B / (ms_step / 1e3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {"partials_avg": round(part_avg, 5), "partials_min": round(min(part_ms), 5),
+                      "partials_max": round(max(part_ms), 5)},
+        "roofline": {"bound": "hbm", "kernel": kernel + "_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(kernel, args.workload)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_int8(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -305,6 +420,9 @@ def main():
     cfg = config(args.workload)
     if cfg["kind"] == "mla":
         main_mla(args, kvd, make_config_inputs)
+        return
+    if cfg["kind"] == "paged_int8":
+        main_int8(args, kvd, make_config_inputs)
         return
     dev = torch.device("cuda:0")
     inp = make_config_inputs(args.workload, sentinel="zero")[0]

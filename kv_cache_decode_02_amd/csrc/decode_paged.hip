@@ -728,7 +728,9 @@ hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
 template <int KT, int D, int HPW>
 hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
   constexpr bool kWide = KT != kF32 || D < 128;  // register budget allows >= 2 waves
-  constexpr int NBUF = (KT != kF32 && HPW == 1) ? 3 : 2;
+  // INT8 buffers are half the registers of bf16 ones: three fit beside four
+  // heads at two waves per SIMD.
+  constexpr int NBUF = (KT == kI8 || (KT == kBF16 && HPW == 1)) ? 3 : 2;
   constexpr int WPE = (HPW == 1 && kWide) ? 3 : (kWide ? 2 : 1);
   const int ratio = a.num_q_heads / a.num_kv_heads;
   if (a.counts) {

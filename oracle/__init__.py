@@ -17,8 +17,8 @@ KV cache.  Citation keys used in this package:
 Modules:
   numerics   exact unpacking of stored bf16 / fp32 values to fp64
   paged      slot mapping, in-place append and logical gather (block table)
-  attention  single-query decode attention, split partials + LSE merge,
-             absorbed MLA, full causal recompute
+  attention  single-query decode attention, sliding-window decode, split
+             partials + LSE merge, absorbed MLA, full causal recompute
   capacity   KV byte accounting (per token, useful / padded / paged, shared)
   quant      INT8 cache: per-channel K / per-token V codes, append, decode
 
@@ -33,6 +33,8 @@ from .attention import (
     decode_attention,
     decode_attention_weights,
     decode_attn_paged,
+    window_start,
+    decode_attn_paged_window,
     split_partials,
     lse_merge,
     decode_attention_split,
@@ -62,6 +64,7 @@ __all__ = [
     "bf16_bits_to_f64", "to_f64",
     "slot_of", "append_paged", "gather_history", "gather_logical",
     "decode_attention", "decode_attention_weights", "decode_attn_paged",
+    "window_start", "decode_attn_paged_window",
     "split_partials", "lse_merge", "decode_attention_split",
     "mla_decode", "mla_decode_paged", "causal_attention",
     "bytes_per_token", "paged_capacity", "unique_block_bytes",

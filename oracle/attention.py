@@ -117,6 +117,48 @@ def decode_attn_paged(q, k_pool, v_pool, block_table, seq_lens, dtype,
     return np.stack(outs)
 
 
+def window_start(length, window):
+    """First visible position of a decode row at position length - 1 under a
+    sliding window of ``window`` positions.
+
+    [DQ] "Window Attention / Sliding Window": only the most recent W tokens'
+    K/V are kept and attended to; [SW] (the note after the worked example):
+    the states outside the window may be dropped because the model's visible
+    range itself is different.  Reading taken: the W most recent positions
+    include the current one, so the row sees [max(0, length - W), length).
+    """
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    return max(0, int(length) - int(window))
+
+
+def decode_attn_paged_window(q, k_pool, v_pool, block_table, seq_lens, dtype, window,
+                             k_new=None, v_new=None, scale=None, block_size=16):
+    """``decode_attn_paged`` restricted to the sliding window: sequence b
+    attends to positions [window_start(seq_lens[b], window), seq_lens[b]).
+    With k_new / v_new the pools hold the history and the new row is the last
+    position, as in ``decode_attn_paged``.  Returns fp64 [B, H_q, dv]."""
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new or neither")
+    lens = np.asarray(seq_lens)
+    outs = []
+    for b in range(lens.shape[0]):
+        n = int(lens[b])
+        start = window_start(n, window)
+        if k_new is not None:
+            K = np.concatenate([
+                to_f64(gather_history(k_pool, block_table, lens, b, block_size), dtype),
+                to_f64(np.asarray(k_new)[b:b + 1], dtype)])
+            V = np.concatenate([
+                to_f64(gather_history(v_pool, block_table, lens, b, block_size), dtype),
+                to_f64(np.asarray(v_new)[b:b + 1], dtype)])
+        else:
+            K = to_f64(gather_logical(k_pool, block_table, b, n, block_size), dtype)
+            V = to_f64(gather_logical(v_pool, block_table, b, n, block_size), dtype)
+        outs.append(decode_attention(to_f64(np.asarray(q)[b], dtype), K[start:], V[start:], scale))
+    return np.stack(outs)
+
+
 def split_partials(q_h, K_g, V_g, scale, partition):
     """Per-partition (m_p, l_p, o_p) of one query head over its K/V head.
 
@@ -227,13 +269,15 @@ def mla_decode_paged(q, c_pool, block_table, seq_lens, d_c, scale, dtype="bf16",
     return np.stack(outs)
 
 
-def causal_attention(Q, K, V, past_len, scale=None):
+def causal_attention(Q, K, V, past_len, scale=None, window=None):
     """Full causal attention of n new rows over past_len cached + n new rows.
 
     Q: [n, d]; K: [past_len + n, d]; V: [past_len + n, dv].  Query row i sees
     key j exactly when j <= past_len + i ([MV] 改动三: ``mask[i, :past_len+i+1]``
     is visible; with past_len = 0 this is the lower-triangular prefill mask,
-    with n = 1 the all-visible decode row).  The whole score matrix is formed,
+    with n = 1 the all-visible decode row).  With ``window`` W, row i also
+    needs j > past_len + i - W (the band of the W most recent positions, [DQ]
+    "Window Attention / Sliding Window").  The whole score matrix is formed,
     masked with -inf and normalised row by row.  Returns [n, dv].
     """
     Q = np.asarray(Q, dtype=np.float64)
@@ -247,6 +291,8 @@ def causal_attention(Q, K, V, past_len, scale=None):
         scale = 1.0 / math.sqrt(d)
     scores = scale * (Q @ K.T)
     visible = np.arange(total)[None, :] <= (past_len + np.arange(n))[:, None]
+    if window is not None:
+        visible &= np.arange(total)[None, :] > (past_len + np.arange(n))[:, None] - window
     scores = np.where(visible, scores, -np.inf)
     scores = scores - scores.max(axis=1, keepdims=True)
     p = np.exp(scores)

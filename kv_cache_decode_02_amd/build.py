@@ -1,6 +1,8 @@
 """Build the HIP decode library for gfx950 in-tree: csrc/* -> libkvdecode.so.
 
-Usage:  python -m kv_cache_decode_02_amd.build  [--jobs N] [--save-temps]
+Usage:  python kv_cache_decode_02_amd/build.py  [--jobs N] [--save-temps]
+
+(Run it as a script: importing the package would load the library it builds.)
 
 Every source is compiled with hipcc for gfx950 only.  Packed fp32 vector
 instructions are disabled for the device code (``-packed-fp32-ops``).

@@ -181,6 +181,35 @@ int decode_attn_merge(void* out, const int32_t* seq_lens, int batch, int num_q_h
                       void* stream);
 
 /*
+ * decode_attn_paged_window -- decode_attn_paged under a sliding window: the
+ * row of sequence b attends to positions [max(0, L - window), L) only, the
+ * most recent `window` tokens including this step's ("KV-Cache——为什么AI回复
+ * 越来越快", Window Attention / Sliding Window; "KV缓存原理与显存估算": the
+ * states outside the window may be dropped because the model's visible range
+ * is different).  Blocks wholly before the window are never read, so their
+ * table entries may be stale; the block holding position L - window must
+ * still hold its positions.
+ *   window  >= 1 (KVD_ERR_SHAPE otherwise); window >= L gives decode_attn_paged
+ * Other arguments, sizes, workspace and errors as for decode_attn_paged; the
+ * partials phase alone is decode_attn_paged_window_partials (finish with
+ * decode_attn_merge, whose arguments do not change).
+ */
+int decode_attn_paged_window(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int batch,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                             float scale, int window, int partition_tokens, void* workspace,
+                             size_t workspace_bytes, kvd_dtype_t dtype, void* stream);
+
+int decode_attn_paged_window_partials(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int max_seq_len, float scale, int window,
+                                      int partition_tokens, void* workspace,
+                                      size_t workspace_bytes, kvd_dtype_t dtype, void* stream);
+
+/*
  * decode_attn_paged_append -- kv_append_paged followed by decode_attn_paged,
  * in one pass over the cache: the decode step of "KV-Cache——为什么AI回复越来越
  * 快" (02: this step's K/V join the cache, then the new query attends to all

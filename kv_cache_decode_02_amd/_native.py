@@ -20,7 +20,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kvdecode.h")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m kv_cache_decode_02_amd.build or __graft_entry__.build())")
+        "(python kv_cache_decode_02_amd/build.py or __graft_entry__.build())")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -64,6 +64,12 @@ lib.decode_attn_paged_int8.restype = _i
 lib.decode_attn_paged_int8.argtypes = [_vp] + _INT8_ARGS
 lib.decode_attn_paged_int8_partials.restype = _i
 lib.decode_attn_paged_int8_partials.argtypes = _INT8_ARGS
+# the paged arguments with `window` after `scale`
+_WINDOW_ARGS = _PAGED_ARGS[:14] + [_i] + _PAGED_ARGS[14:]
+lib.decode_attn_paged_window.restype = _i
+lib.decode_attn_paged_window.argtypes = [_vp] + _WINDOW_ARGS
+lib.decode_attn_paged_window_partials.restype = _i
+lib.decode_attn_paged_window_partials.argtypes = _WINDOW_ARGS
 lib.decode_attn_merge.restype = _i
 lib.decode_attn_merge.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]
 
@@ -196,6 +202,38 @@ def decode_attn_paged_partials(q, k_cache, v_cache, block_table, seq_lens, max_s
     args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
                        partition_tokens, workspace)
     _check(lib.decode_attn_paged_partials(*args, _stream(stream)), "decode_attn_paged_partials")
+
+
+def decode_attn_paged_window(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, window,
+                             scale=None, partition_tokens=0, workspace=None, out=None,
+                             stream=None):
+    """decode_attn_paged under a sliding window: each row attends to its
+    last ``window`` positions; returns out."""
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    if workspace is None:
+        workspace = alloc_workspace(B, h_q, h_kv, d, max_seq_len, partition_tokens,
+                                    device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype)
+    args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+                       partition_tokens, workspace)
+    args = args[:14] + [int(window)] + args[14:]
+    _check(lib.decode_attn_paged_window(_ptr(out), *args, _stream(stream)),
+           "decode_attn_paged_window")
+    return out
+
+
+def decode_attn_paged_window_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
+                                      window, workspace, scale=None, partition_tokens=0,
+                                      stream=None):
+    """First phase of decode_attn_paged_window; finish with decode_attn_merge."""
+    args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+                       partition_tokens, workspace)
+    args = args[:14] + [int(window)] + args[14:]
+    _check(lib.decode_attn_paged_window_partials(*args, _stream(stream)),
+           "decode_attn_paged_window_partials")
 
 
 def _append_args(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens, max_seq_len, scale,

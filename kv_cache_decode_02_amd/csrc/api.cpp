@@ -244,6 +244,7 @@ static PagedLaunch paged_launch(const void* q, const void* k_cache, const void* 
   a.int8 = false;
   a.k_scale = nullptr;
   a.v_scale = nullptr;
+  a.window = 0;
   return a;
 }
 
@@ -327,6 +328,52 @@ int decode_attn_paged(void* out, const void* q, const void* k_cache, const void*
   const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
                                      workspace, dtype, s);
   return hip_status(launch_merge(m, st));
+}
+
+int decode_attn_paged_window_partials(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int max_seq_len, float scale, int window,
+                                      int partition_tokens, void* workspace,
+                                      size_t workspace_bytes, kvd_dtype_t dtype, void* stream) {
+  Sizes s;
+  const int rc = check_paged(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                             num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                             max_seq_len, partition_tokens, workspace, workspace_bytes, dtype, &s);
+  if (rc) return rc;
+  if (window < 1) return KVD_ERR_SHAPE;
+  if (batch == 0) return KVD_OK;
+  PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                               num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
+                               max_seq_len, scale, workspace, dtype, s);
+  a.window = window;
+  return hip_status(launch_paged_partials(a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_paged_window(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int batch,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                             int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                             float scale, int window, int partition_tokens, void* workspace,
+                             size_t workspace_bytes, kvd_dtype_t dtype, void* stream) {
+  Sizes s;
+  int rc = check_paged(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                       max_seq_len, partition_tokens, workspace, workspace_bytes, dtype, &s);
+  if (rc) return rc;
+  if (window < 1) return KVD_ERR_SHAPE;
+  if (batch == 0) return KVD_OK;
+  if (!out) return KVD_ERR_NULL;
+  rc = decode_attn_paged_window_partials(q, k_cache, v_cache, block_table, seq_lens, batch,
+                                         num_q_heads, num_kv_heads, head_dim, block_size,
+                                         max_blocks_per_seq, num_blocks, max_seq_len, scale,
+                                         window, partition_tokens, workspace, workspace_bytes,
+                                         dtype, stream);
+  if (rc) return rc;
+  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
+                                     workspace, dtype, s);
+  return hip_status(launch_merge(m, static_cast<hipStream_t>(stream)));
 }
 
 int decode_attn_paged_append_partials(const void* q, void* k_cache, void* v_cache,

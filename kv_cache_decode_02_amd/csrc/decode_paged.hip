@@ -192,13 +192,13 @@ __device__ __forceinline__ void load_block(Frag<KT, D>& f, const PagedLaunch& a,
                    KT == kI8 ? a.v_scale + blk0 * a.num_kv_heads : nullptr);
 }
 
-// One block through the online softmax of HPW heads; nvalid tokens count.
-template <int KT, int D, int HPW, bool PBF16>
+// One block through the online softmax of HPW heads; tokens [nskip, nvalid)
+// of the block count.
+template <int KT, int D, int HPW>
 __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
                                               const uint32_t (&qv)[HPW][RowShape<KT, D>::QW],
-                                              int lane, int nvalid, float sl2,
+                                              int lane, int nskip, int nvalid, float sl2,
                                               HeadState<HPW, D / 8>& st) {
-  static_assert(KT != kF32 || !PBF16, "bf16 weights need a 16- or 8-bit cache");
   using S = RowShape<KT, D>;
   constexpr int W = S::W, DPL = S::DPL;
   const int grp = lane >> 3;
@@ -229,7 +229,7 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
   }
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok) {
-    const bool ok = grp + 8 * tok < nvalid;
+    const bool ok = grp + 8 * tok >= nskip && grp + 8 * tok < nvalid;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
       float part = 0.f;
@@ -251,16 +251,6 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
   }
   // Rows past the valid tokens were read as zeros: weight 0 times value 0.
   const uint32_t (&vw)[2][W] = f.v;
-  // For bf16 weights: the V elements of the lane's two tokens, paired per
-  // dimension (shared by all heads of the group).
-  uint32_t vlo[PBF16 ? W : 1], vhi[PBF16 ? W : 1];
-  if constexpr (KT == kBF16) {
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      vlo[w] = pair_lo(vw[0][w], vw[1][w]);
-      vhi[w] = pair_hi(vw[0][w], vw[1][w]);
-    }
-  }
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
     const float mx = fmaxf(s[0][h], s[1][h]);
@@ -283,18 +273,10 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
       const uint32_t pp = pack_f16x2(p0 * f.vs[0], p1 * f.vs[1]);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[h][e] = dot2_f16(pp, vp[e], acc[h][e]);
-    } else if constexpr (PBF16) {
-      // Weights rounded to bf16 and paired over the lane's two tokens; the
-      // same rounded weights feed the sum, so the output stays an exact
-      // convex combination of V rows.  Products accumulate in fp32.
-      const uint32_t pp = pack_bf16x2(p0, p1);
-      l[h] = dot2_bf16(pp, kBf16OnePair, l[h]);
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        acc[h][2 * w] = dot2_bf16(pp, vlo[w], acc[h][2 * w]);
-        acc[h][2 * w + 1] = dot2_bf16(pp, vhi[w], acc[h][2 * w + 1]);
-      }
     } else {
+      // fp32 weights and products.  (bf16 weights, paired for dot2, halve
+      // this work but their 8-bit rounding costs up to ~2e-3 absolute on
+      // outputs that cancel to near zero over a few positions.)
       l[h] += p0 + p1;
 #pragma unroll
       for (int w = 0; w < W; ++w) {
@@ -346,17 +328,18 @@ __device__ __forceinline__ void merge_groups(HeadState<HPW, DPL>& st) {
 }
 
 // Streams blocks [j_begin, j_end) of sequence b through the online softmax of
-// query heads h0 .. h0 + HPW - 1, which all read KV head g; tokens at or past
-// t_end carry no weight.  Block ids are read 64 at a time, one per lane, and
+// query heads h0 .. h0 + HPW - 1, which all read KV head g; tokens before
+// t_start or at or past t_end carry no weight.  Block ids are read 64 at a
+// time, one per lane, and
 // broadcast with readlane.  On return the lane groups are merged.
 // With `fused` (the range ends at the sequence's last position t_end - 1 and
 // this step's K/V rows are given): that position is taken from k_new / v_new
 // instead of the cache, as the last token of the softmax, and when
 // `write_new` the wave also stores KV head g's part of the rows into their
 // cache slot (the append of the same step).
-template <int KT, int D, int HPW, int NBUF, bool PBF16>
+template <int KT, int D, int HPW, int NBUF>
 __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, int g, int h0,
-                                       int j_begin, int j_end, int t_end,
+                                       int j_begin, int j_end, int t_start, int t_end,
                                        HeadState<HPW, D / 8>& st, bool fused = false,
                                        bool write_new = false) {
   uint32_t qv[HPW][RowShape<KT, D>::QW];
@@ -394,7 +377,9 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
         if (jj < nblk) {
           int nv;
           block_of(jj, nv);
-          softmax_block<KT, D, HPW, PBF16>(buf[s0], qv, lane, nv, sl2, st);
+          softmax_block<KT, D, HPW>(buf[s0], qv, lane,
+                                           max(0, t_start - (c0 + jj) * kBlockTokens), nv, sl2,
+                                           st);
         }
         int nv;
         const int blk = block_of(jj + NBUF, nv);
@@ -413,7 +398,7 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
       Frag<KT, D> f;
       load_rows<KT, D>(f, static_cast<const uint32_t*>(a.k_new) + src,
                          static_cast<const uint32_t*>(a.v_new) + src, a, lane, g, 1);
-      softmax_block<KT, D, HPW, PBF16>(f, qv, lane, 1, sl2, st);
+      softmax_block<KT, D, HPW>(f, qv, lane, 0, 1, sl2, st);
       if (write_new && lane < 8) {
         const size_t dst = (static_cast<size_t>(blk) * kBlockTokens + t_last % kBlockTokens) * row_words +
                            g * S::RW;
@@ -484,23 +469,30 @@ __device__ __forceinline__ void write_partial(const PagedLaunch& a, int lane, si
   }
 }
 
-// Blocks of sequence b that hold positions (lengths clamped to max_seq_len).
+// First position a decode row of length len sees: 0, or with a sliding
+// window of W positions max(0, len - W) ("KV-Cache——为什么AI回复越来越快",
+// Window Attention / Sliding Window: only the most recent W tokens count).
+__device__ __forceinline__ int first_visible(const PagedLaunch& a, int len) {
+  return a.window > 0 ? max(0, len - a.window) : 0;
+}
+
+// Blocks of sequence b that hold visible positions (lengths clamped to
+// max_seq_len), from block first_visible / 16 on.
 __device__ __forceinline__ int seq_blocks(const PagedLaunch& a, int b) {
   const int len = min(a.seq_lens[b], a.max_seq_len);
-  return len > 0 ? (len + kBlockTokens - 1) / kBlockTokens : 0;
+  if (len <= 0) return 0;
+  return (len + kBlockTokens - 1) / kBlockTokens - first_visible(a, len) / kBlockTokens;
 }
 
 // NBUF: register buffers per wave (NBUF - 1 blocks in flight during compute).
 // WPE: waves per SIMD the register allocation is sized for.
-// PBF16: softmax weights enter the V product as bf16 pairs (dot2, fp32
-// accumulation) instead of fp32 FMAs; only for bf16 caches.
 //
 // Fixed partitions: one wavefront per unit (b, partition, kv head g, chunk of
 // HPW query heads).  WG: wavefronts per workgroup.  Consecutive units are the
 // KV heads (and head chunks) of one (sequence, partition), so a workgroup's
 // waves read the same blocks together: for 8 KV heads an 8-wave workgroup
 // reads whole contiguous token rows of every block.
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_partials_kernel(PagedLaunch a) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -519,17 +511,26 @@ void paged_partials_kernel(PagedLaunch a) {
 
   int len = a.seq_lens[b];
   len = min(len, a.max_seq_len);
-  const int t_begin = p * a.partition_tokens;
-  if (len <= t_begin) return;
-  const int t_end = min(len, t_begin + a.partition_tokens);
-  const int j0 = t_begin / kBlockTokens;
-  const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
+  const int p_begin = p * a.partition_tokens;
+  if (len <= p_begin) return;
+  const int t_end = min(len, p_begin + a.partition_tokens);
+  const int t_begin = max(p_begin, first_visible(a, len));
   const int h0 = g * ratio + hc * HPW;
-
-  HeadState<HPW, D / 8> st;
-  const bool fused = a.k_new != nullptr && t_end == len;
-  attend<KT, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + nblk, t_end, st, fused, hc == 0);
   const size_t P = a.num_partitions;
+  HeadState<HPW, D / 8> st;
+  if (t_begin >= t_end) {
+    // Before a sliding window: an empty piece (l = 0), which the merge skips.
+    reset_state(st);
+    write_partial<KT, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P,
+                              pick_group(st, lane));
+    return;
+  }
+  const int j0 = t_begin / kBlockTokens;
+  const int nblk = (t_end + kBlockTokens - 1) / kBlockTokens - j0;
+
+  const bool fused = a.k_new != nullptr && t_end == len;
+  attend<KT, D, HPW, NBUF>(a, lane, b, g, h0, j0, j0 + nblk, t_begin, t_end, st, fused,
+                                  hc == 0);
   write_partial<KT, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P,
                               pick_group(st, lane));
 }
@@ -550,7 +551,7 @@ void paged_partials_kernel(PagedLaunch a) {
 // segment's first item), and the workgroup of piece 0 records the number of
 // pieces for the merge.  Pieces of one (b, h) never exceed ceil(blocks /
 // kMinPieceBlocks) + 1.
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_balanced_kernel(PagedLaunch a) {
   // [batch + 1] blocks of the sequences before b, then [batch + 1] count of
@@ -667,9 +668,11 @@ void paged_balanced_kernel(PagedLaunch a) {
       const int g = u / hchunks, hc = u % hchunks;
       const int h0 = g * ratio + hc * HPW;
       const int t_end = wave_uniform(min(a.seq_lens[b], a.max_seq_len));
+      const int t_start = first_visible(a, t_end);
+      const int js = t_start / kBlockTokens;  // the sequence's first visible block
       const bool fused = a.k_new != nullptr && seg_end == seg_begin + nb;
-      attend<KT, D, HPW, NBUF, PBF16>(a, lane, b, g, h0, j0, j0 + (seg_end - item), t_end, st,
-                                        fused, hc == 0);
+      attend<KT, D, HPW, NBUF>(a, lane, b, g, h0, js + j0, js + j0 + (seg_end - item),
+                                      t_start, t_end, st, fused, hc == 0);
       const int first = owner(vpos(b, ug, nb, 0));
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
@@ -699,24 +702,24 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = (KT != kF32)>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
 hipError_t launch_variant(const PagedLaunch& a, hipStream_t stream) {
   const int ratio = a.num_q_heads / a.num_kv_heads;
   const long long units = static_cast<long long>(a.batch) * a.num_partitions * a.num_kv_heads *
                           (ratio / HPW);
   const long long blocks = (units + WG - 1) / WG;
-  hipLaunchKernelGGL((paged_partials_kernel<KT, D, HPW, NBUF, WPE, WG, PBF16>),
+  hipLaunchKernelGGL((paged_partials_kernel<KT, D, HPW, NBUF, WPE, WG>),
                      dim3(static_cast<unsigned>(blocks)), dim3(64 * WG), 0, stream, a);
   return hipGetLastError();
 }
 
 // Balanced split: as many workgroups as are resident at once (4 * WPE
 // wavefronts per compute unit, in workgroups of WG waves).
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG, bool PBF16 = (KT != kF32)>
+template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
 hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
   const size_t lds = 2 * static_cast<size_t>(a.batch + 1) * sizeof(int);
   const int groups = device_cus() * ((4 * WPE) / WG);
-  hipLaunchKernelGGL((paged_balanced_kernel<KT, D, HPW, NBUF, WPE, WG, PBF16>),
+  hipLaunchKernelGGL((paged_balanced_kernel<KT, D, HPW, NBUF, WPE, WG>),
                      dim3(static_cast<unsigned>(groups)), dim3(64 * WG), lds, stream, a);
   return hipGetLastError();
 }

@@ -51,6 +51,8 @@ struct PagedLaunch {
   bool int8;
   const float* k_scale;
   const float* v_scale;
+  // Sliding window: each row sees its last `window` positions; 0 = all.
+  int window;
 };
 
 struct MergeLaunch {

@@ -220,3 +220,13 @@ def test_decode_int8_rejections():
     assert paged_int8(d=96) == EUNSUP
     assert paged_int8(ws=None) == EWS
     assert paged_int8(B=0, o=None, ks=None, vs=None, ws=None, wsb=0) == OK
+
+
+def test_window_rejections():
+    f = lib.decode_attn_paged_window
+    args = [P, P, P, P, P, P, 2, 32, 8, 128, 16, 64, 128, 1024, 0.088]
+    tail = [0, P, 1 << 40, 1, None]
+    assert f(*args, 0, *tail) == ESHAPE      # window must be >= 1
+    assert f(*args, -5, *tail) == ESHAPE
+    assert f(*args[:1], None, *args[2:], 16, *tail) == ENULL
+    assert f(*args[:6], 0, *args[7:], 16, *tail) == OK  # empty batch

@@ -65,7 +65,8 @@ enum {
     KVD_ERR_SHAPE = -2,       /* sizes inconsistent or out of range */
     KVD_ERR_UNSUPPORTED = -3, /* dtype, head_dim, block_size or head ratio not built */
     KVD_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required */
-    KVD_ERR_HIP = -5          /* the HIP runtime reported a launch error */
+    KVD_ERR_HIP = -5,         /* the HIP runtime reported a launch error */
+    KVD_ERR_NOMEM = -6        /* block pool: too few free blocks, or host memory */
 };
 
 /* Static English text for a status code (never NULL). */
@@ -357,6 +358,83 @@ int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const 
                                     int max_seq_len, float scale, int partition_tokens,
                                     void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
                                     void* stream);
+
+/*
+ * kv_copy_blocks -- copy whole physical blocks of one cache tensor: for each
+ * pair i, block pairs[2 i] is copied onto block pairs[2 i + 1] (the copy a
+ * copy-on-write append needs before it writes; see kvd_seq_append).
+ *   cache       [num_blocks] blocks of block_bytes each (any element type;
+ *               call once per tensor: K, V, and an INT8 cache's V scales)
+ *   pairs       device int32 [num_pairs][2]; pairs naming a block outside
+ *               [0, num_blocks) are skipped; destinations must be distinct and
+ *               no destination may be another pair's source
+ *   block_bytes a multiple of 4
+ */
+int kv_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, size_t block_bytes,
+                   int num_blocks, void* stream);
+
+/*
+ * Host-side paged block allocator ("KV-Cache——为什么AI回复越来越快", 08
+ * PagedAttention: fixed-size pages, freed pages reused at once,
+ * copy-on-write sharing of a common prefix; "KV Cache（键值缓存）", 2.3:
+ * block tables, reference counts and copy-on-write between parallel samples;
+ * "KV缓存原理与显存估算", 知识点三 and 源码导读: chained block hashes that
+ * carry the whole prefix and a compatibility identity, reference counts for
+ * who holds a block, hashes for what it holds).  Plain host memory; not
+ * thread-safe (one pool per scheduler thread).  Every call succeeds
+ * completely or changes nothing.
+ *
+ * Blocks carry a reference count.  A block whose count drops to zero is free
+ * again; if it holds a registered hash it stays matchable until it is reused,
+ * and blocks that never held a hash are reused first, then cached ones in
+ * the order they were released.
+ */
+typedef struct kvd_block_pool kvd_block_pool;
+
+/* Chained hashes of the full blocks of a token sequence: h_0 = SHA-256 of
+ * (tag, identity, block tokens), h_j = SHA-256 of (tag, h_{j-1}, identity,
+ * block tokens), tokens and lengths as little-endian 32-bit words.  Writes 32
+ * bytes per full block to `out` and returns their number (a partial last
+ * block gets none); tokens must be >= 0.  `identity` is any byte string
+ * naming what makes cached states compatible (model, adapter, tokenizer,
+ * dtype, salt). */
+int kvd_block_hashes(const int32_t* tokens, int64_t num_tokens, int block_size,
+                     const void* identity, size_t identity_bytes, uint8_t* out);
+
+kvd_block_pool* kvd_pool_create(int num_blocks, int block_size); /* NULL on bad sizes */
+void kvd_pool_destroy(kvd_block_pool* pool);
+int kvd_pool_available(const kvd_block_pool* pool);  /* blocks an append may take */
+int kvd_pool_used(const kvd_block_pool* pool);       /* blocks with count > 0 */
+int kvd_pool_block_ref(const kvd_block_pool* pool, int block);
+
+/* Sequences are small integers. */
+int kvd_seq_create(kvd_block_pool* pool);           /* empty sequence */
+int kvd_seq_fork(kvd_block_pool* pool, int seq);    /* shares every block (count + 1) */
+int kvd_seq_release(kvd_block_pool* pool, int seq); /* count - 1 on each of its blocks */
+int64_t kvd_seq_len(const kvd_block_pool* pool, int seq);
+/* The block table; returns the number of blocks (capacity must hold them). */
+int kvd_seq_table(const kvd_block_pool* pool, int seq, int32_t* out, int capacity);
+
+/* Reserves slots for num_tokens more positions.  If the last block is partly
+ * filled and shared, it is first replaced by a fresh block: the pair (old,
+ * new) goes to copies[0..1] and *num_copies = 1, and the caller copies the
+ * block's contents (kv_copy_blocks) before writing the new positions.  New
+ * blocks are taken as needed.  KVD_ERR_NOMEM when the pool cannot supply
+ * them (nothing changes). */
+int kvd_seq_append(kvd_block_pool* pool, int seq, int num_tokens, int32_t* copies,
+                   int max_copies, int* num_copies);
+
+/* Registers the first num_hashes full blocks of seq under the given block
+ * hashes (kvd_block_hashes of its tokens), so later sequences can reuse
+ * them.  A block that already holds a hash, and a hash another block holds,
+ * are left as they are. */
+int kvd_seq_commit_hashes(kvd_block_pool* pool, int seq, const uint8_t* hashes, int num_hashes);
+
+/* A new sequence that reuses the longest chain of registered blocks matching
+ * hashes[0..], which is hashed, written-once state: *num_hit blocks, length
+ * num_hit * block_size; the caller computes the positions after them. */
+int kvd_seq_create_with_prefix(kvd_block_pool* pool, const uint8_t* hashes, int num_hashes,
+                               int* num_hit);
 
 #ifdef __cplusplus
 }

@@ -70,6 +70,33 @@ lib.decode_attn_paged_window.restype = _i
 lib.decode_attn_paged_window.argtypes = [_vp] + _WINDOW_ARGS
 lib.decode_attn_paged_window_partials.restype = _i
 lib.decode_attn_paged_window_partials.argtypes = _WINDOW_ARGS
+lib.kv_copy_blocks.restype = _i
+lib.kv_copy_blocks.argtypes = [_vp, _vp, _i, _sz, _i, _vp]
+_i64 = ctypes.c_int64
+lib.kvd_block_hashes.restype = _i
+lib.kvd_block_hashes.argtypes = [_vp, _i64, _i, _vp, _sz, _vp]
+lib.kvd_pool_create.restype = _vp
+lib.kvd_pool_create.argtypes = [_i, _i]
+lib.kvd_pool_destroy.restype = None
+lib.kvd_pool_destroy.argtypes = [_vp]
+for _name in ("kvd_pool_available", "kvd_pool_used", "kvd_seq_create"):
+    getattr(lib, _name).restype = _i
+    getattr(lib, _name).argtypes = [_vp]
+lib.kvd_pool_block_ref.restype = _i
+lib.kvd_pool_block_ref.argtypes = [_vp, _i]
+for _name in ("kvd_seq_fork", "kvd_seq_release"):
+    getattr(lib, _name).restype = _i
+    getattr(lib, _name).argtypes = [_vp, _i]
+lib.kvd_seq_len.restype = _i64
+lib.kvd_seq_len.argtypes = [_vp, _i]
+lib.kvd_seq_table.restype = _i
+lib.kvd_seq_table.argtypes = [_vp, _i, _vp, _i]
+lib.kvd_seq_append.restype = _i
+lib.kvd_seq_append.argtypes = [_vp, _i, _i, _vp, _i, _vp]
+lib.kvd_seq_commit_hashes.restype = _i
+lib.kvd_seq_commit_hashes.argtypes = [_vp, _i, _vp, _i]
+lib.kvd_seq_create_with_prefix.restype = _i
+lib.kvd_seq_create_with_prefix.argtypes = [_vp, _vp, _i, _vp]
 lib.decode_attn_merge.restype = _i
 lib.decode_attn_merge.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]
 
@@ -431,3 +458,108 @@ def decode_attn_paged_int8_partials(q, k_cache, v_cache, k_scale, v_scale, block
                       scale, partition_tokens, workspace)
     _check(lib.decode_attn_paged_int8_partials(*args, _stream(stream)),
            "decode_attn_paged_int8_partials")
+
+
+# --- block copies and the host block pool ----------------------------------------
+
+def kv_copy_blocks(cache, pairs, stream=None):
+    """Copy whole blocks of ``cache`` [num_blocks, ...]: block pairs[i, 0] onto
+    block pairs[i, 1] (device int32 [n, 2])."""
+    _need(cache, "cache")
+    _need(pairs, "pairs", dtype=torch.int32)
+    n = pairs.shape[0] if pairs.numel() else 0
+    nb = cache.shape[0]
+    block_bytes = cache[0].numel() * cache.element_size()
+    _check(lib.kv_copy_blocks(_ptr(cache), _ptr(pairs), n, block_bytes, nb, _stream(stream)),
+           "kv_copy_blocks")
+
+
+def block_hashes(tokens, block_size, identity=b""):
+    """Chained 32-byte keys of the full blocks of a token list (host)."""
+    toks = (ctypes.c_int32 * max(1, len(tokens)))(*[int(t) for t in tokens])
+    full = len(tokens) // block_size if block_size > 0 else 0
+    out = (ctypes.c_uint8 * max(1, 32 * full))()
+    ident = ctypes.create_string_buffer(bytes(identity), max(1, len(identity)))
+    r = lib.kvd_block_hashes(toks, len(tokens), block_size, ident, len(identity), out)
+    _check(min(r, 0), "kvd_block_hashes")
+    raw = bytes(out)
+    return [raw[32 * j:32 * (j + 1)] for j in range(r)]
+
+
+class PoolExhausted(KvdError):
+    """The block pool has too few free blocks for the request."""
+
+
+class BlockPool:
+    """Host-side paged block allocator (reference counts, fork, copy-on-write,
+    prefix reuse through chained block keys); see include/kvdecode.h."""
+
+    def __init__(self, num_blocks, block_size=16):
+        self._p = lib.kvd_pool_create(num_blocks, block_size)
+        if not self._p:
+            raise KvdError("kvd_pool_create: invalid sizes or out of memory")
+        self.block_size = block_size
+
+    def close(self):
+        if self._p:
+            lib.kvd_pool_destroy(self._p)
+            self._p = None
+
+    def __del__(self):
+        self.close()
+
+    def _ok(self, r, what):
+        if r == -6:
+            raise PoolExhausted(f"{what}: {lib.kvd_status_string(r).decode()}")
+        _check(min(r, 0), what)
+        return r
+
+    def available(self):
+        return self._ok(lib.kvd_pool_available(self._p), "kvd_pool_available")
+
+    def used(self):
+        return self._ok(lib.kvd_pool_used(self._p), "kvd_pool_used")
+
+    def ref(self, block):
+        return self._ok(lib.kvd_pool_block_ref(self._p, block), "kvd_pool_block_ref")
+
+    def create(self):
+        return self._ok(lib.kvd_seq_create(self._p), "kvd_seq_create")
+
+    def fork(self, seq):
+        return self._ok(lib.kvd_seq_fork(self._p, seq), "kvd_seq_fork")
+
+    def release(self, seq):
+        self._ok(lib.kvd_seq_release(self._p, seq), "kvd_seq_release")
+
+    def length(self, seq):
+        r = lib.kvd_seq_len(self._p, seq)
+        self._ok(min(r, 0), "kvd_seq_len")
+        return r
+
+    def table(self, seq):
+        n = self.length(seq) // self.block_size + 1
+        buf = (ctypes.c_int32 * max(1, n))()
+        r = self._ok(lib.kvd_seq_table(self._p, seq, buf, n), "kvd_seq_table")
+        return list(buf[:r])
+
+    def append(self, seq, num_tokens):
+        """Reserve num_tokens slots; returns the (old, new) block copies to do first."""
+        pairs = (ctypes.c_int32 * 2)()
+        n = ctypes.c_int(0)
+        self._ok(lib.kvd_seq_append(self._p, seq, num_tokens, pairs, 1, ctypes.byref(n)),
+                 "kvd_seq_append")
+        return [(pairs[0], pairs[1])] if n.value else []
+
+    def commit(self, seq, keys):
+        raw = b"".join(keys)
+        buf = ctypes.create_string_buffer(raw, max(1, len(raw)))
+        self._ok(lib.kvd_seq_commit_hashes(self._p, seq, buf, len(keys)), "kvd_seq_commit_hashes")
+
+    def create_with_prefix(self, keys):
+        raw = b"".join(keys)
+        buf = ctypes.create_string_buffer(raw, max(1, len(raw)))
+        hit = ctypes.c_int(0)
+        s = self._ok(lib.kvd_seq_create_with_prefix(self._p, buf, len(keys), ctypes.byref(hit)),
+                     "kvd_seq_create_with_prefix")
+        return s, hit.value

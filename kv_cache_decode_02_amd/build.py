@@ -23,7 +23,8 @@ LIB_NAME = "libkvdecode.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "append.hip", "decode_paged.hip", "decode_merge.hip", "decode_mla.hip"]
+SOURCES = ["api.cpp", "block_pool.cpp", "append.hip", "decode_paged.hip", "decode_merge.hip",
+           "decode_mla.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}"]

@@ -138,6 +138,7 @@ const char* kvd_status_string(int status) {
     case KVD_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block_size or head ratio";
     case KVD_ERR_WORKSPACE: return "workspace is NULL or too small";
     case KVD_ERR_HIP: return "HIP runtime error";
+    case KVD_ERR_NOMEM: return "block pool exhausted or host allocation failed";
     default: return "unknown status";
   }
 }
@@ -524,6 +525,22 @@ int decode_attn_paged_int8(void* out, const void* q, const int8_t* k_cache, cons
   const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
                                      workspace, dtype, s);
   return hip_status(launch_merge(m, static_cast<hipStream_t>(stream)));
+}
+
+int kv_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, size_t block_bytes,
+                   int num_blocks, void* stream) {
+  if (num_pairs < 0 || num_blocks < 1 || block_bytes == 0 || block_bytes % 4 != 0)
+    return KVD_ERR_SHAPE;
+  if (num_pairs == 0) return KVD_OK;
+  if (!cache || !pairs) return KVD_ERR_NULL;
+  CopyBlocksLaunch a;
+  a.cache = cache;
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  a.block_bytes = block_bytes;
+  a.vec16 = aligned16(cache) && block_bytes % 16 == 0;
+  return hip_status(launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
 static int mla_setup(const void* q, const void* c_cache, const int32_t* block_table,

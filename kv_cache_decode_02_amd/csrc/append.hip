@@ -109,7 +109,32 @@ hipError_t launch_append_int8_typed(const AppendInt8Launch& a, hipStream_t strea
   return hipGetLastError();
 }
 
+// Whole-block copies for copy-on-write: workgroup i copies pair i, as 16-byte
+// words when the block size allows, else 4-byte words.
+template <int VEC>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksLaunch a) {
+  const int32_t src = a.pairs[2 * blockIdx.x], dst = a.pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  const size_t words = a.block_bytes / 4;
+  const uint32_t* s = static_cast<const uint32_t*>(a.cache) + static_cast<size_t>(src) * words;
+  uint32_t* d = static_cast<uint32_t*>(a.cache) + static_cast<size_t>(dst) * words;
+  for (size_t w = threadIdx.x * VEC; w < words; w += blockDim.x * VEC) {
+    uint32_t tmp[VEC];
+    load_words<VEC>(tmp, s + w);
+    store_words<VEC>(d + w, tmp);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksLaunch& a, hipStream_t stream) {
+  if (a.vec16) {
+    hipLaunchKernelGGL(copy_blocks_kernel<4>, dim3(a.num_pairs), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(copy_blocks_kernel<1>, dim3(a.num_pairs), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream) {
   return a.bf16 ? launch_append_int8_typed<true>(a, stream) : launch_append_int8_typed<false>(a, stream);

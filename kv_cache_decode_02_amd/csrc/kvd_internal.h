@@ -92,6 +92,14 @@ struct AppendInt8Launch {
   bool bf16;
 };
 
+struct CopyBlocksLaunch {
+  void* cache;
+  const int32_t* pairs;  // device [num_pairs][2]
+  int num_pairs, num_blocks;
+  size_t block_bytes;
+  bool vec16;  // cache 16-byte aligned and block_bytes a multiple of 16
+};
+
 struct MlaLaunch {
   const void* q;            // [B, H, d_c + d_rope] bf16
   const void* c_cache;      // [NB, 16, d_c + d_rope] bf16
@@ -107,6 +115,7 @@ struct MlaLaunch {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream);
 hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksLaunch& a, hipStream_t stream);
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 hipError_t launch_mla_partials(const MlaLaunch& a, hipStream_t stream);

@@ -21,6 +21,7 @@ Modules:
              partials + LSE merge, absorbed MLA, full causal recompute
   capacity   KV byte accounting (per token, useful / padded / paged, shared)
   quant      INT8 cache: per-channel K / per-token V codes, append, decode
+  allocator  block pool model: counts, fork, copy-on-write, chained keys
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against values
 printed on the pages (``tests/golden/``), closed forms, invariants and special
@@ -52,6 +53,7 @@ from .quant import (
     decode_attn_paged_int8,
     history_int8,
 )
+from .allocator import block_hashes, BlockPool, PoolExhausted
 from .capacity import (
     bytes_per_token,
     paged_capacity,
@@ -71,4 +73,5 @@ __all__ = [
     "kv_cache_bytes", "mla_elements_per_token",
     "quantize", "token_scale", "channel_scales", "append_paged_int8", "dequantize_k",
     "dequantize_v", "decode_attn_paged_int8", "history_int8",
+    "block_hashes", "BlockPool", "PoolExhausted",
 ]

@@ -29,7 +29,7 @@ cases.  No function here is "parity unpinned".
 """
 
 from .numerics import bf16_bits_to_f64, to_f64
-from .paged import slot_of, append_paged, gather_history, gather_logical
+from .paged import slot_of, append_paged, append_paged_multi, gather_history, gather_logical
 from .attention import (
     decode_attention,
     decode_attention_weights,
@@ -42,6 +42,7 @@ from .attention import (
     mla_decode,
     mla_decode_paged,
     causal_attention,
+    prefill_attn_paged,
 )
 from .quant import (
     quantize,
@@ -64,11 +65,11 @@ from .capacity import (
 
 __all__ = [
     "bf16_bits_to_f64", "to_f64",
-    "slot_of", "append_paged", "gather_history", "gather_logical",
+    "slot_of", "append_paged", "append_paged_multi", "gather_history", "gather_logical",
     "decode_attention", "decode_attention_weights", "decode_attn_paged",
     "window_start", "decode_attn_paged_window",
     "split_partials", "lse_merge", "decode_attention_split",
-    "mla_decode", "mla_decode_paged", "causal_attention",
+    "mla_decode", "mla_decode_paged", "causal_attention", "prefill_attn_paged",
     "bytes_per_token", "paged_capacity", "unique_block_bytes",
     "kv_cache_bytes", "mla_elements_per_token",
     "quantize", "token_scale", "channel_scales", "append_paged_int8", "dequantize_k",

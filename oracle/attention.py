@@ -298,3 +298,36 @@ def causal_attention(Q, K, V, past_len, scale=None, window=None):
     p = np.exp(scores)
     p = p / p.sum(axis=1, keepdims=True)
     return p @ V
+
+
+def prefill_attn_paged(q_rows, k_pool, v_pool, block_table, seq_lens, cu_rows, dtype,
+                       scale=None, block_size=16):
+    """Causal attention of n_b new rows per sequence over a paged cache that
+    already holds every position [0, seq_lens[b]) (history and the new rows).
+
+    Row i of sequence b sits at position p = seq_lens[b] - n_b + i and sees
+    positions 0..p ([MV] 改动三: mask[i, :past_len + i + 1] is visible; with
+    past_len = 0 the lower triangle of prefill, with n_b = 1 the decode row;
+    [SW] 知识点二: each new query attends to the cache plus the new rows before
+    it).  q_rows: [N, H_q, d] stored values in row order of cu_rows; returns
+    fp64 [N, H_q, d].  Heads share K/V in contiguous groups as in
+    ``decode_attention``.
+    """
+    cu = np.asarray(cu_rows)
+    q_rows = np.asarray(q_rows)
+    N, H_q, _ = q_rows.shape
+    H_kv = np.asarray(k_pool).shape[2]
+    r = H_q // H_kv
+    out = np.zeros((N, H_q, np.asarray(v_pool).shape[3]), dtype=np.float64)
+    for b, length in enumerate(np.asarray(seq_lens)):
+        n = int(cu[b + 1] - cu[b])
+        if n == 0:
+            continue
+        L = int(length)
+        K = to_f64(gather_logical(k_pool, block_table, b, L, block_size), dtype)
+        V = to_f64(gather_logical(v_pool, block_table, b, L, block_size), dtype)
+        Q = to_f64(q_rows[cu[b]:cu[b] + n], dtype)
+        for h in range(H_q):
+            out[cu[b]:cu[b] + n, h] = causal_attention(Q[:, h], K[:, h // r], V[:, h // r],
+                                                      past_len=L - n, scale=scale)
+    return out

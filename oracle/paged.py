@@ -87,3 +87,29 @@ def gather_logical(pool, block_table, b, length, block_size=16):
 def gather_history(pool, block_table, seq_lens, b, block_size=16):
     """The cached history of sequence b: positions [0, seq_lens[b] - 1)."""
     return gather_logical(pool, block_table, b, int(seq_lens[b]) - 1, block_size)
+
+
+def append_paged_multi(k_pool, v_pool, k_rows, v_rows, cu_rows, block_table, seq_lens,
+                       block_size=16):
+    """Write n_b new rows per sequence, n_b = cu_rows[b + 1] - cu_rows[b],
+    into positions [seq_lens[b] - n_b, seq_lens[b]) (seq_lens counts them, as
+    for the single-row append); return new pools.
+
+    The many-slot form of the in-place write ([MV] 生产系统的做法; [SW] 知识点二:
+    prefill writes the prompt's rows, decode appends one per step).  k_rows /
+    v_rows: [N, H_kv, d] in row order of cu_rows.
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    cu = np.asarray(cu_rows)
+    nb = k_out.shape[0]
+    for b, length in enumerate(np.asarray(seq_lens)):
+        n = int(cu[b + 1] - cu[b])
+        if n > int(length):
+            raise ValueError("more new rows than positions")
+        for i in range(n):
+            blk, off = slot_of(block_table, b, int(length) - n + i, block_size)
+            _check_block(blk, nb)
+            k_out[blk, off] = k_rows[cu[b] + i]
+            v_out[blk, off] = v_rows[cu[b] + i]
+    return k_out, v_out

@@ -14,6 +14,8 @@ from .gen import (
     make_paged_decode,
     PagedInt8Inputs,
     make_paged_decode_int8,
+    PagedPrefillInputs,
+    make_paged_prefill,
     make_mla,
     BLOCK_SIZE,
     UNUSED_TABLE_ENTRY,
@@ -22,7 +24,7 @@ from .configs import CONFIGS, config, make_config_inputs
 
 __all__ = [
     "PagedDecodeInputs", "MlaInputs", "bf16_round_bits", "make_paged_decode",
-    "PagedInt8Inputs", "make_paged_decode_int8",
+    "PagedInt8Inputs", "make_paged_decode_int8", "PagedPrefillInputs", "make_paged_prefill",
     "make_mla", "BLOCK_SIZE", "UNUSED_TABLE_ENTRY", "CONFIGS", "config",
     "make_config_inputs",
 ]

@@ -305,3 +305,76 @@ def make_paged_decode_int8(rng, B, H_q, H_kv, d, seq_lens, table="permuted", std
     _mark_unfilled(vs, owned, lens, block_size, scale)
     return PagedInt8Inputs(B, H_q, H_kv, d, block_size, lens.astype(np.int32), bt, nb, q, kq, vq,
                            vs, ks, k_new, v_new)
+
+
+@dataclass
+class PagedPrefillInputs:
+    dtype: str
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    block_size: int
+    seq_lens: np.ndarray     # int32 [B]: history + new rows
+    cu_rows: np.ndarray      # int32 [B + 1]: new rows of sequence b are cu[b] .. cu[b+1]-1
+    block_table: np.ndarray
+    num_blocks: int
+    q: np.ndarray            # [N, H_q, d]
+    k_pool: np.ndarray       # [NB, 16, H_kv, d], history filled
+    v_pool: np.ndarray
+    k_new: np.ndarray        # [N, H_kv, d]
+    v_new: np.ndarray
+
+    @property
+    def max_blocks_per_seq(self):
+        return int(self.block_table.shape[1])
+
+    @property
+    def max_seq_len(self):
+        return int(self.seq_lens.max())
+
+    @property
+    def max_rows(self):
+        return int(np.max(np.diff(self.cu_rows))) if self.B else 0
+
+    @property
+    def num_rows(self):
+        return int(self.cu_rows[-1])
+
+
+def make_paged_prefill(rng, B, H_q, H_kv, d, past_lens, new_lens, dtype="bf16",
+                       table="permuted", std=1.0, sentinel="nan", block_size=BLOCK_SIZE):
+    """Chunked prefill / multi-token decode inputs: sequence b holds past_lens[b]
+    cached rows and appends new_lens[b] rows this call (queries for each).
+    Draw order: block permutation, q, K pool, V pool, k_new, v_new.  Slots of
+    the new rows and the unused tail hold the sentinel."""
+    past = np.asarray(past_lens, dtype=np.int64)
+    new = np.asarray(new_lens, dtype=np.int64)
+    if past.shape != (B,) or new.shape != (B,) or np.any(past < 0) or np.any(new < 0):
+        raise ValueError("past_lens and new_lens must have B non-negative entries")
+    lens = past + new
+    if np.any(lens < 1):
+        raise ValueError("every sequence needs at least one position")
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    mb = _blocks_needed(lens.max(), block_size)
+    bt, nb, owned = _assign_blocks(rng, lens, block_size, mb, table)
+    N = int(new.sum())
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(new)
+    q = _draw(rng, (N, H_q, d), std, dtype)
+    k_pool = _draw(rng, (nb, block_size, H_kv, d), std, dtype)
+    v_pool = _draw(rng, (nb, block_size, H_kv, d), std, dtype)
+    k_new = _draw(rng, (N, H_kv, d), std, dtype)
+    v_new = _draw(rng, (N, H_kv, d), std, dtype)
+    if sentinel is not None:
+        val = _sentinel(dtype, sentinel)
+        for blocks, p in zip(owned, past):
+            # every slot from position p on is unfilled
+            for j, blk in enumerate(blocks):
+                start = max(0, int(p) - j * block_size)
+                if start < block_size:
+                    k_pool[int(blk), start:] = val
+                    v_pool[int(blk), start:] = val
+    return PagedPrefillInputs(dtype, B, H_q, H_kv, d, block_size, lens.astype(np.int32), cu, bt,
+                              nb, q, k_pool, v_pool, k_new, v_new)

@@ -360,6 +360,45 @@ int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const 
                                     void* stream);
 
 /*
+ * Chunked prefill and multi-token decode ("单请求 KV Cache", 改动三: a row at
+ * position past_len + i sees mask[i, :past_len + i + 1], the prefill triangle
+ * for past_len = 0 and the decode row for one new token; "KV缓存原理与显存估算",
+ * 知识点二: the new rows join the cache, then each query attends to it).
+ * Sequence b has n_b = cu_rows[b + 1] - cu_rows[b] new rows, stored in row
+ * order in q / k_new / v_new, and seq_lens[b] counts them.
+ *
+ * kv_append_paged_multi -- writes the n_b new K/V rows [N, num_kv_heads,
+ * head_dim] to positions [seq_lens[b] - n_b, seq_lens[b]) through the block
+ * table, as kv_append_paged does for one.  max_rows >= every n_b (sizes the
+ * grid); rows of a sequence with n_b > seq_lens[b], or whose block lies
+ * outside the pool, are not written.
+ */
+int kv_append_paged_multi(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                          const int32_t* cu_rows, const int32_t* block_table,
+                          const int32_t* seq_lens, int batch, int max_rows, int num_kv_heads,
+                          int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                          kvd_dtype_t dtype, void* stream);
+
+/*
+ * prefill_attn_paged -- causal attention of the new rows: row i of sequence b
+ * (position p = seq_lens[b] - n_b + i) gets softmax(scale q . K[0..p]) V[0..p]
+ * per query head (K/V head h / (num_q_heads / num_kv_heads)).  The cache must
+ * already hold all seq_lens[b] positions (kv_append_paged_multi first).
+ *   q, out     [N, num_q_heads, head_dim] bf16 (dtype KVD_BF16), 16-byte aligned
+ *   head_dim   64 or 128
+ *   max_rows   >= every n_b, <= max_seq_len
+ * Both products run on bf16 MFMA with fp32 accumulation; the softmax weights
+ * enter as a bf16 value plus its bf16 remainder (~16 bits).  Other arguments
+ * and errors as for decode_attn_paged (no workspace).
+ */
+int prefill_attn_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cu_rows, const int32_t* block_table,
+                       const int32_t* seq_lens, int batch, int max_rows, int num_q_heads,
+                       int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                       int num_blocks, int max_seq_len, float scale, kvd_dtype_t dtype,
+                       void* stream);
+
+/*
  * kv_copy_blocks -- copy whole physical blocks of one cache tensor: for each
  * pair i, block pairs[2 i] is copied onto block pairs[2 i + 1] (the copy a
  * copy-on-write append needs before it writes; see kvd_seq_append).

@@ -31,6 +31,8 @@ from ._native import (
     decode_attn_paged_int8,
     decode_attn_paged_int8_partials,
     kv_copy_blocks,
+    kv_append_paged_multi,
+    prefill_attn_paged,
     block_hashes,
     BlockPool,
     PoolExhausted,
@@ -45,6 +47,7 @@ __all__ = [
     "decode_attn_merge", "decode_attn_workspace_bytes", "decode_attn_partition_tokens",
     "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials", "mla_default_scale",
     "kv_append_paged_int8", "decode_attn_paged_int8", "decode_attn_paged_int8_partials",
-    "kv_copy_blocks", "block_hashes", "BlockPool", "PoolExhausted",
+    "kv_copy_blocks", "kv_append_paged_multi", "prefill_attn_paged", "block_hashes",
+    "BlockPool", "PoolExhausted",
     "LIB_PATH", "HEADER_PATH",
 ]

@@ -97,6 +97,10 @@ lib.kvd_seq_commit_hashes.restype = _i
 lib.kvd_seq_commit_hashes.argtypes = [_vp, _i, _vp, _i]
 lib.kvd_seq_create_with_prefix.restype = _i
 lib.kvd_seq_create_with_prefix.argtypes = [_vp, _vp, _i, _vp]
+lib.kv_append_paged_multi.restype = _i
+lib.kv_append_paged_multi.argtypes = [_vp] * 7 + [_i] * 8 + [_vp]
+lib.prefill_attn_paged.restype = _i
+lib.prefill_attn_paged.argtypes = [_vp] * 7 + [_i] * 9 + [_f, _i, _vp]
 lib.decode_attn_merge.restype = _i
 lib.decode_attn_merge.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]
 
@@ -563,3 +567,48 @@ class BlockPool:
         s = self._ok(lib.kvd_seq_create_with_prefix(self._p, buf, len(keys), ctypes.byref(hit)),
                      "kvd_seq_create_with_prefix")
         return s, hit.value
+
+
+# --- chunked prefill / multi-token decode ----------------------------------------
+
+def kv_append_paged_multi(k_cache, v_cache, k_new, v_new, cu_rows, block_table, seq_lens,
+                          max_rows, stream=None):
+    """Write n_b = cu_rows[b+1] - cu_rows[b] new rows of each sequence into
+    positions [seq_lens[b] - n_b, seq_lens[b]); k_new/v_new: [N, H_kv, d]."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, dtype=k_cache.dtype)
+    for t, n in ((cu_rows, "cu_rows"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need(t, n, dtype=torch.int32)
+    nb, bs, h_kv, d = k_cache.shape
+    B = seq_lens.shape[0]
+    status = lib.kv_append_paged_multi(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                       _ptr(cu_rows), _ptr(block_table), _ptr(seq_lens), B,
+                                       int(max_rows), h_kv, d, bs, block_table.shape[1], nb,
+                                       _dtype_code(k_cache), _stream(stream))
+    _check(status, "kv_append_paged_multi")
+
+
+def prefill_attn_paged(q, k_cache, v_cache, cu_rows, block_table, seq_lens, max_seq_len,
+                       max_rows, scale=None, out=None, stream=None):
+    """Causal attention of the new rows q [N, H_q, d] (bf16) over the paged
+    cache, which already holds them; returns out [N, H_q, d]."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, dtype=torch.bfloat16)
+    for t, n in ((cu_rows, "cu_rows"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need(t, n, dtype=torch.int32)
+    N, h_q, d = q.shape
+    nb, bs, h_kv, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise KvdError("q, k_cache and v_cache head sizes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=torch.bfloat16)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    B = seq_lens.shape[0]
+    status = lib.prefill_attn_paged(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(cu_rows), _ptr(block_table), _ptr(seq_lens), B,
+                                    int(max_rows), h_q, h_kv, d, bs, block_table.shape[1], nb,
+                                    int(max_seq_len), float(scale), KVD_BF16, _stream(stream))
+    _check(status, "prefill_attn_paged")
+    return out

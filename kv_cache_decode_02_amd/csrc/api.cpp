@@ -543,6 +543,81 @@ int kv_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, size_t bloc
   return hip_status(launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
+int kv_append_paged_multi(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                          const int32_t* cu_rows, const int32_t* block_table,
+                          const int32_t* seq_lens, int batch, int max_rows, int num_kv_heads,
+                          int head_dim, int block_size, int max_blocks_per_seq, int num_blocks,
+                          kvd_dtype_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return KVD_ERR_UNSUPPORTED;
+  if (batch < 0 || max_rows < 0 || num_kv_heads < 1 || head_dim < 1 || head_dim > 1024)
+    return KVD_ERR_SHAPE;
+  if (block_size != kBlockSize) return KVD_ERR_UNSUPPORTED;
+  if (max_blocks_per_seq < 1 || max_blocks_per_seq > kMaxTableBlocks || num_blocks < 1)
+    return KVD_ERR_SHAPE;
+  const long long row_bytes = static_cast<long long>(num_kv_heads) * head_dim * elem_bytes(dtype);
+  if (row_bytes % 4 != 0 || row_bytes / 4 > INT_MAX) return KVD_ERR_SHAPE;
+  if (batch == 0 || max_rows == 0) return KVD_OK;
+  if (batch > 65535 || max_rows > INT_MAX / 2) return KVD_ERR_SHAPE;
+  if (!k_cache || !v_cache || !k_new || !v_new || !cu_rows || !block_table || !seq_lens)
+    return KVD_ERR_NULL;
+  AppendMultiLaunch a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cu_rows = cu_rows;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.max_rows = max_rows;
+  a.row_words = static_cast<int>(row_bytes / 4);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.vec16 = aligned16(k_cache) && aligned16(v_cache) && aligned16(k_new) && aligned16(v_new);
+  return hip_status(launch_append_multi(a, static_cast<hipStream_t>(stream)));
+}
+
+int prefill_attn_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* cu_rows, const int32_t* block_table,
+                       const int32_t* seq_lens, int batch, int max_rows, int num_q_heads,
+                       int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                       int num_blocks, int max_seq_len, float scale, kvd_dtype_t dtype,
+                       void* stream) {
+  if (!dtype_ok(dtype)) return KVD_ERR_UNSUPPORTED;
+  int rc = check_heads(batch, num_q_heads, num_kv_heads);
+  if (rc) return rc;
+  if (!prefill_supported(head_dim, dtype == KVD_BF16)) return KVD_ERR_UNSUPPORTED;
+  rc = check_table(block_size, max_blocks_per_seq, num_blocks, max_seq_len);
+  if (rc) return rc;
+  if (max_rows < 0 || max_rows > max_seq_len) return KVD_ERR_SHAPE;
+  if (batch > 65535 || num_kv_heads > 65535) return KVD_ERR_SHAPE;
+  const long long r = num_q_heads / num_kv_heads;
+  if ((static_cast<long long>(max_rows) * r + 63) / 64 > INT_MAX) return KVD_ERR_SHAPE;
+  if (batch == 0 || max_rows == 0) return KVD_OK;
+  if (!out || !q || !k_cache || !v_cache || !cu_rows || !block_table || !seq_lens)
+    return KVD_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return KVD_ERR_SHAPE;
+  PrefillLaunch a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.cu_rows = cu_rows;
+  a.out = out;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_seq_len = max_seq_len;
+  a.max_rows = max_rows;
+  a.scale = scale;
+  return hip_status(launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 static int mla_setup(const void* q, const void* c_cache, const int32_t* block_table,
                      const int32_t* seq_lens, int batch, int num_q_heads, int d_c, int d_rope,
                      int block_size, int max_blocks_per_seq, int num_blocks, int max_seq_len,

@@ -125,7 +125,43 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksLaunch a) {
   }
 }
 
+// Many-slot append: workgroup (i, b, tensor) writes new row i of sequence b
+// to position seq_lens[b] - n_b + i.
+template <int VEC>
+__global__ __launch_bounds__(256) void append_multi_kernel(AppendMultiLaunch a) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  const bool is_v = blockIdx.z == 1;
+  const int r0 = a.cu_rows[b];
+  const int n = a.cu_rows[b + 1] - r0;
+  if (i >= n) return;
+  const int len = a.seq_lens[b];
+  const long long cap = static_cast<long long>(a.max_blocks_per_seq) * kBlockTokens;
+  if (n > len || len > cap) return;  // violated precondition: write nothing
+  const int pos = len - n + i;
+  const int blk = a.block_table[static_cast<size_t>(b) * a.max_blocks_per_seq + pos / kBlockTokens];
+  if (blk < 0 || blk >= a.num_blocks) return;
+  uint32_t* cache = static_cast<uint32_t*>(is_v ? a.v_cache : a.k_cache);
+  const uint32_t* src = static_cast<const uint32_t*>(is_v ? a.v_new : a.k_new) +
+                        static_cast<size_t>(r0 + i) * a.row_words;
+  uint32_t* dst = cache + (static_cast<size_t>(blk) * kBlockTokens + pos % kBlockTokens) * a.row_words;
+  for (int w = threadIdx.x * VEC; w < a.row_words; w += blockDim.x * VEC) {
+    uint32_t tmp[VEC];
+    load_words<VEC>(tmp, src + w);
+    store_words<VEC>(dst + w, tmp);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_multi(const AppendMultiLaunch& a, hipStream_t stream) {
+  const dim3 grid(a.max_rows, a.batch, 2);
+  if (a.vec16 && a.row_words % 4 == 0) {
+    hipLaunchKernelGGL(append_multi_kernel<4>, grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(append_multi_kernel<1>, grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_copy_blocks(const CopyBlocksLaunch& a, hipStream_t stream) {
   if (a.vec16) {

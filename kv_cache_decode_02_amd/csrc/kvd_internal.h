@@ -100,6 +100,31 @@ struct CopyBlocksLaunch {
   bool vec16;  // cache 16-byte aligned and block_bytes a multiple of 16
 };
 
+struct PrefillLaunch {
+  const void* q;            // [N, H_q, D] bf16, rows of sequence b are cu_rows[b] ..
+  const void* k_cache;      // [NB, 16, H_kv, D] bf16
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;  // positions including the new rows
+  const int32_t* cu_rows;   // [B + 1]
+  void* out;                // [N, H_q, D] bf16
+  int batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, max_seq_len;
+  int max_rows;             // bound on rows per sequence (sizes the grid)
+  float scale;
+};
+
+struct AppendMultiLaunch {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;        // [N, H_kv, D]
+  const void* v_new;
+  const int32_t* cu_rows;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int batch, max_rows, row_words, max_blocks_per_seq, num_blocks;
+  bool vec16;
+};
+
 struct MlaLaunch {
   const void* q;            // [B, H, d_c + d_rope] bf16
   const void* c_cache;      // [NB, 16, d_c + d_rope] bf16
@@ -116,6 +141,9 @@ struct MlaLaunch {
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream);
 hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksLaunch& a, hipStream_t stream);
+hipError_t launch_append_multi(const AppendMultiLaunch& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillLaunch& a, hipStream_t stream);
+bool prefill_supported(int head_dim, bool bf16);
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const MergeLaunch& a, hipStream_t stream);
 hipError_t launch_mla_partials(const MlaLaunch& a, hipStream_t stream);

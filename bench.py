@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_llama3_8b",
                     choices=["gqa_llama3_8b", "mha_llama2_7b", "long_gqa_split", "tiny",
-                             "mla_deepseek_v2", "gqa_llama3_8b_int8"])
+                             "mla_deepseek_v2", "gqa_llama3_8b_int8", "prefill_llama3_8b"])
     ap.add_argument("--replicas", type=int, default=4,
                     help="MLA: rotate over this many copies of the latent cache so the "
                          "timed reads come from HBM, not the 256 MB Infinity Cache")
@@ -326,6 +326,122 @@ def main_int8(args, kvd, make_config_inputs):
     print(json.dumps(res), flush=True)
 
 
+def prefill_flops(inp):
+    """Algorithmic FLOPs of the causal prefill: every row's q.K and P.V over
+    the positions it sees (2 d multiply-adds per position and head each)."""
+    n = np.diff(inp.cu_rows).astype(np.int64)
+    past = inp.seq_lens.astype(np.int64) - n
+    seen = int(np.sum(n * past + n * (n + 1) // 2))
+    return seen * inp.H_q * inp.d * 4
+
+
+def cpu_baseline_prefill(inp, target_s):
+    """Time the fp64 oracle on rows of the prefill chunks (in order, sequence
+    by sequence) until ~target_s; reports FLOP/s on the same count."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    rows = seen = 0
+    r = inp.H_q // inp.H_kv
+    k2, v2 = oracle.append_paged_multi(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new,
+                                       inp.cu_rows, inp.block_table, inp.seq_lens)
+    for b in range(inp.B):
+        n = int(inp.cu_rows[b + 1] - inp.cu_rows[b])
+        L = int(inp.seq_lens[b])
+        K = oracle.to_f64(oracle.gather_logical(k2, inp.block_table, b, L), inp.dtype)
+        V = oracle.to_f64(oracle.gather_logical(v2, inp.block_table, b, L), inp.dtype)
+        for i in range(n):
+            p = L - n + i
+            q = oracle.to_f64(inp.q[inp.cu_rows[b] + i], inp.dtype)
+            oracle.decode_attention(q, K[:p + 1], V[:p + 1])
+            rows += 1
+            seen += p + 1
+            if time.perf_counter() - t0 > target_s:
+                break
+        if time.perf_counter() - t0 > target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": seen * inp.H_q * inp.d * 4 / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} prefill rows (all {inp.H_q} heads, {seen} visible positions) in "
+                      f"{dt:.1f} s; fp64 numpy on {os.cpu_count()} host CPUs"}
+
+
+def main_prefill(args, kvd, make_config_inputs):
+    """One chunked-prefill call: the many-slot append and the causal MFMA
+    kernel, timed like the decode step (graph replay, events around the
+    attention kernel)."""
+    import torch
+    dev = torch.device("cuda:0")
+    inp = make_config_inputs(args.workload, sentinel="zero")[0]
+    q, kc, vc = up(inp.q, dev), up(inp.k_pool, dev), up(inp.v_pool, dev)
+    kn, vn = up(inp.k_new, dev), up(inp.v_new, dev)
+    cu, table, seq = up(inp.cu_rows, dev), up(inp.block_table, dev), up(inp.seq_lens, dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    L, R = inp.max_seq_len, inp.max_rows
+
+    def step(ev=None):
+        kvd.kv_append_paged_multi(kc, vc, kn, vn, cu, table, seq, R)
+        if ev is not None:
+            ev[0].record(stream)
+        kvd.prefill_attn_paged(q, kc, vc, cu, table, seq, L, R, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_eager = start.elapsed_time(end) / args.steps
+    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_avg = float(np.mean(part_ms))
+    ms_step, graph_check = ms_eager, None
+    if not args.no_graph:
+        ms_step, graph_check = time_graph(torch, step, out, args)
+    flops = prefill_flops(inp)
+    value = flops / (ms_step / 1e3) / 1e12
+    achieved = flops / (part_avg / 1e3) / 1e12
+    res = {
+        "metric": "chunked-prefill attention TFLOP/s (bf16 MFMA), paged GQA, 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "step_launch": "hip graph" if not args.no_graph else "eager",
+        "step_kernels": "kv_append_paged_multi, prefill", "ms_per_step_eager": round(ms_eager, 5),
+        "graph_replays_match_eager": graph_check, "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": inp.H_q,
+                   "num_kv_heads": inp.H_kv, "head_dim": inp.d, "block_size": 16,
+                   "new_rows": inp.num_rows, "seq_lens": inp.seq_lens.tolist()},
+        "tokens_per_s": round(inp.num_rows / (ms_step / 1e3), 1),
+        "flops_per_step": flops,
+        "wall_s_timed": round(wall, 4),
+        "kernel_ms": {"prefill_avg": round(part_avg, 5), "prefill_min": round(min(part_ms), 5),
+                      "prefill_max": round(max(part_ms), 5)},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic("prefill", args.workload)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -423,6 +539,9 @@ def main():
         return
     if cfg["kind"] == "paged_int8":
         main_int8(args, kvd, make_config_inputs)
+        return
+    if cfg["kind"] == "prefill":
+        main_prefill(args, kvd, make_config_inputs)
         return
     dev = torch.device("cuda:0")
     inp = make_config_inputs(args.workload, sentinel="zero")[0]

@@ -83,3 +83,31 @@ def test_sequence_without_new_rows_is_skipped():
     ref = oracle.prefill_attn_paged(inp.q, k2, v2, inp.block_table, inp.seq_lens, inp.cu_rows,
                                     "bf16")
     assert_contract(down_f64(out), ref, "empty chunk")
+
+
+def test_prefill_full_size_sampled():
+    name = "prefill_llama3_8b"
+    log(f"full {name}: generating")
+    from workloads import make_config_inputs
+    inp = make_config_inputs(name)[0]
+    dev = Dev(inp)
+    dev.append()
+    out = kvd.prefill_attn_paged(dev.q, dev.k, dev.v, dev.cu, dev.table, dev.seq,
+                                 inp.max_seq_len, inp.max_rows)
+    torch.cuda.synchronize()
+    got = down_f64(out)
+    assert np.all(np.isfinite(got))
+    k2, v2 = oracle.append_paged_multi(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new,
+                                       inp.cu_rows, inp.block_table, inp.seq_lens)
+    rng = np.random.default_rng(6)
+    for b in range(inp.B):
+        n = int(inp.cu_rows[b + 1] - inp.cu_rows[b])
+        L = int(inp.seq_lens[b])
+        K = oracle.to_f64(oracle.gather_logical(k2, inp.block_table, b, L), "bf16")
+        V = oracle.to_f64(oracle.gather_logical(v2, inp.block_table, b, L), "bf16")
+        for i in [0, n - 1, int(rng.integers(n))]:
+            p = L - n + i
+            row = inp.cu_rows[b] + i
+            ref = oracle.decode_attention(oracle.to_f64(inp.q[row], "bf16"), K[:p + 1], V[:p + 1])
+            assert_contract(got[row], ref, f"{name} b={b} row={i}")
+    log(f"full {name}: ok")

@@ -17,15 +17,20 @@
                   the gqa_llama3_8b batch (same seed, so the same lengths)
                   over an INT8 cache: per-channel K and per-token V scales,
                   bf16 queries and output
+  prefill_llama3_8b
+                  chunked prefill on the Llama-3-8B shape (H_q = 32, H_kv =
+                  8, d_head = 128): 4 sequences with 0 / 2048 / 4096 / 6144
+                  cached positions each take a 2048-token chunk, bf16 N(0,1)
 
-Seeds: config k (1..5 in the order above) uses numpy default_rng(42 + k); 42
+Seeds: config k (1..5 in the order above, 6 for the prefill) uses numpy
+default_rng(42 + k), the INT8 batch the GQA batch's seed; 42
 is the seed of the pages' own numpy sketch.  Lengths are drawn first, then the
 generator's fixed draw order (``workloads.gen``).
 """
 
 import numpy as np
 
-from .gen import make_paged_decode, make_paged_decode_int8, make_mla
+from .gen import make_paged_decode, make_paged_decode_int8, make_paged_prefill, make_mla
 
 CONFIGS = {
     "tiny": dict(index=1, kind="paged", B=1, H_q=4, H_kv=4, d=32, layers=2,
@@ -46,6 +51,9 @@ CONFIGS = {
     "gqa_llama3_8b_int8": dict(index=3, kind="paged_int8", B=64, H_q=32, H_kv=8, d=128,
                                layers=1, lens=("uniform", 512, 8192), dtype="int8",
                                table="permuted", std=1.0, partition=0),
+    "prefill_llama3_8b": dict(index=6, kind="prefill", B=4, H_q=32, H_kv=8, d=128, layers=1,
+                              lens=("list", (0, 2048, 4096, 6144)), new=2048, dtype="bf16",
+                              table="permuted", std=1.0, partition=0),
 }
 
 
@@ -84,6 +92,11 @@ def make_config_inputs(name, sentinel="nan", rng=None):
             layers.append(make_paged_decode(rng, B, cfg["H_q"], cfg["H_kv"], cfg["d"], lens,
                                             dtype=cfg["dtype"], table=cfg["table"],
                                             std=cfg["std"], sentinel=sentinel))
+        elif cfg["kind"] == "prefill":
+            layers.append(make_paged_prefill(rng, B, cfg["H_q"], cfg["H_kv"], cfg["d"], lens,
+                                             [cfg["new"]] * B, dtype=cfg["dtype"],
+                                             table=cfg["table"], std=cfg["std"],
+                                             sentinel=sentinel))
         elif cfg["kind"] == "paged_int8":
             layers.append(make_paged_decode_int8(rng, B, cfg["H_q"], cfg["H_kv"], cfg["d"], lens,
                                                  table=cfg["table"], std=cfg["std"],

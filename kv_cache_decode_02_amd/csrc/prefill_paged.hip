@@ -9,7 +9,7 @@
 // 回复越来越快", 08 PagedAttention).  Unlike one decode row, a chunk of rows
 // reuses every K/V tile many times, so both products are dense contractions.
 //
-// Work decomposition: a workgroup of 4 waves takes 64 "rows" of one (sequence,
+// Work decomposition: a workgroup of 8 waves takes 128 "rows" of one (sequence,
 // KV head g): row rho = (token t of the chunk, head hh of the group) with
 // rho = t * r + hh, so the r query heads that share g's K/V are rows of the
 // same tiles.  K/V stream through LDS in 32-token tiles (two 16-token blocks,
@@ -32,8 +32,9 @@ namespace kvd {
 namespace {
 
 constexpr int kPTile = 32;        // tokens per K/V tile
-constexpr int kPRows = 64;        // rows per workgroup (16 per wave)
-constexpr int kPThreads = 256;
+constexpr int kPWaves = 8;
+constexpr int kPRows = 16 * kPWaves;  // rows per workgroup (16 per wave)
+constexpr int kPThreads = 64 * kPWaves;
 constexpr float kPRaise = 8.0f;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 pbf16x8_t;
@@ -71,9 +72,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillLaunch a) {
   constexpr int RB = D * 2;            // bytes of one token row of one head
   constexpr int LROW = RB + 16;        // padded LDS row
   constexpr int CPT = RB / 16;         // 16-byte chunks per token row
-  constexpr int LOADS = kPTile * CPT / kPThreads;  // chunks per thread per tensor
-  static_assert(LOADS * kPThreads == kPTile * CPT, "tile load split");
-  static_assert(kPThreads % (16 * CPT) == 0 || LOADS == 1, "a load instruction covers one block");
+  constexpr int CHUNKS = kPTile * CPT;  // 16-byte chunks per tile and tensor
+  constexpr int LOADS = (CHUNKS + kPThreads - 1) / kPThreads;  // per thread
+  static_assert(CHUNKS % 64 == 0 && (CHUNKS % kPThreads == 0 || CHUNKS < kPThreads),
+                "whole waves load");
+  static_assert((16 * CPT) % 64 == 0, "a wave's chunks lie in one block");
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kPTile * LROW];
   __shared__ __attribute__((aligned(16))) uint8_t vtile[2][kPTile * LROW];
 
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillLaunch a) {
   float l_lane = 0.f;
   const float sl2 = a.scale * kLog2e;
 
-  // Tile loads: chunk c = tid + 256 u of the tile is token c / CPT, 16 bytes
+  // Tile loads: chunk c = tid + kPThreads u of the tile is token c / CPT, 16 bytes
   // c % CPT of its row; every load instruction stays inside one 16-token
   // block, addressed by a wave-uniform buffer resource whose byte count ends
   // after the block's last position (later rows read as zeros).
@@ -130,6 +133,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillLaunch a) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + kPThreads * u;
+      if (CHUNKS < kPThreads && wave * 64 >= CHUNKS) break;  // waves past the tile
       const int tt = c / CPT, ch = c % CPT;
       const int j = wave_uniform((kPTile * ti + tt) / kBlockTokens);  // block of the sequence
       const int blk = j < a.max_blocks_per_seq && j * kBlockTokens < L ? wave_uniform(trow[j]) : -1;
@@ -150,6 +154,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillLaunch a) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int c = tid + kPThreads * u;
+      if (CHUNKS < kPThreads && wave * 64 >= CHUNKS) break;
       const int tt = c / CPT, ch = c % CPT;
       *reinterpret_cast<uint4*>(&ktile[buf][tt * LROW + 16 * ch]) =
           make_uint4(kreg[u][0], kreg[u][1], kreg[u][2], kreg[u][3]);

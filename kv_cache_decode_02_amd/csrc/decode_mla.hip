@@ -29,10 +29,10 @@
 //            Every lane ends with one head and 8 tokens.
 //   Softmax: online per head with a lazily raised reference max (raised only
 //            when a score exceeds it by more than kRaise log2 units); weights
-//            are rounded to bf16 for the MFMA, and the running sum is taken
-//            from the same rounded weights.  Both waves of a pair compute the
+//            enter the MFMA as a bf16 value plus its bf16 remainder, the
+//            running sum takes them in fp32.  Both waves of a pair compute the
 //            same weights from the same summed scores.
-//   Output:  O^T[256 x 16] += C_tile^T[256 x 32] . P^T[32 x 16] as 16 MFMA
+//   Output:  O^T[256 x 16] += C_tile^T[256 x 32] . P^T[32 x 16] as 2 x 16 MFMA
 //            16x16x32; the A operand (one latent column per lane, tokens
 //            along K) is read from the token-major tile with LDS transpose
 //            loads, and each lane's accumulator column is its own head, so
@@ -277,18 +277,24 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       m_run = mn;
     }
     // Weights as the B operand: K-slot j < 4 is token 4 kb + j, j >= 4 is
-    // token 16 + 4 kb + (j - 4).
-    uint32_t pw[4];
+    // token 16 + 4 kb + (j - 4); a bf16 high part and its bf16 remainder
+    // (about 16 bits of weight: 8-bit weights move outputs that cancel over a
+    // few positions by ~1e-3); the sum takes the fp32 weights.
+    uint32_t pw[4], pr[4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const float p0 = exp2_fast(z[mt][0] - m_run), p1 = exp2_fast(z[mt][1] - m_run);
-      const float p2 = exp2_fast(z[mt][2] - m_run), p3 = exp2_fast(z[mt][3] - m_run);
-      pw[2 * mt] = pack_bf16x2(p0, p1);
-      pw[2 * mt + 1] = pack_bf16x2(p2, p3);
-      l_lane = dot2_bf16(pw[2 * mt], kBf16OnePair, l_lane);
-      l_lane = dot2_bf16(pw[2 * mt + 1], kBf16OnePair, l_lane);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float p0 = exp2_fast(z[mt][2 * h2] - m_run);
+        const float p1 = exp2_fast(z[mt][2 * h2 + 1] - m_run);
+        l_lane += p0 + p1;
+        const uint32_t w = pack_bf16x2(p0, p1);
+        pw[2 * mt + h2] = w;
+        pr[2 * mt + h2] = pack_bf16x2(p0 - bf16_lo(w), p1 - bf16_hi(w));
+      }
     }
     const bf16x8_t pb = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+    const bf16x8_t prb = as_bf16x8(pr[0], pr[1], pr[2], pr[3]);
     // Values as the A operand: lane (col, kb) of the transpose load supplies
     // row T + col / 4 and latent columns 16 nt + 4 (col % 4) .. + 3, which
     // leaves the lane with tokens 4 kb .. +3 (and 16 + 4 kb .. +3) of latent
@@ -305,7 +311,9 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       // Whole-vector casts: K-slots 0-3 from v0, 4-7 from v1.
       const uint2 w0 = __builtin_bit_cast(uint2, v0);
       const uint2 w1 = __builtin_bit_cast(uint2, v1);
-      acc[nt] = mfma16(as_bf16x8(w0.x, w0.y, w1.x, w1.y), pb, acc[nt]);
+      const bf16x8_t va = as_bf16x8(w0.x, w0.y, w1.x, w1.y);
+      acc[nt] = mfma16(va, pb, acc[nt]);
+      acc[nt] = mfma16(va, prb, acc[nt]);
     }
   };
 

@@ -335,6 +335,13 @@ def prefill_flops(inp):
     return seen * inp.H_q * inp.d * 4
 
 
+def prefill_min_bytes(inp):
+    """Least HBM bytes the prefill kernel can move: K and V of every cached
+    position once per KV head, the queries read and the outputs written."""
+    kv = int(inp.seq_lens.astype(np.int64).sum()) * inp.H_kv * inp.d * 2 * 2
+    return kv + 2 * inp.num_rows * inp.H_q * inp.d * 2
+
+
 def cpu_baseline_prefill(inp, target_s):
     """Time the fp64 oracle on rows of the prefill chunks (in order, sequence
     by sequence) until ~target_s; reports FLOP/s on the same count."""
@@ -428,6 +435,7 @@ def main_prefill(args, kvd, make_config_inputs):
                    "new_rows": inp.num_rows, "seq_lens": inp.seq_lens.tolist()},
         "tokens_per_s": round(inp.num_rows / (ms_step / 1e3), 1),
         "flops_per_step": flops,
+        "min_bytes_per_step": prefill_min_bytes(inp),
         "wall_s_timed": round(wall, 4),
         "kernel_ms": {"prefill_avg": round(part_avg, 5), "prefill_min": round(min(part_ms), 5),
                       "prefill_max": round(max(part_ms), 5)},

@@ -76,10 +76,11 @@ struct RowShape {
 };
 
 // Running softmax state of HPW query heads; each lane holds its D / 8
-// dimensions of every accumulator.
+// dimensions of every accumulator.  INT8 cache: vb[h] is the sum of the
+// weights that met biased V codes since the bias was last taken out of acc.
 template <int HPW, int DPL>
 struct HeadState {
-  float m[HPW], l[HPW], acc[HPW][DPL];
+  float m[HPW], l[HPW], vb[HPW], acc[HPW][DPL];
 };
 
 template <int HPW, int DPL>
@@ -88,8 +89,44 @@ __device__ __forceinline__ void reset_state(HeadState<HPW, DPL>& st) {
   for (int h = 0; h < HPW; ++h) {
     st.m[h] = kMinusBig;
     st.l[h] = 0.f;
+    st.vb[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) st.acc[h][e] = 0.f;
+  }
+}
+
+// INT8 codes as fp16 numbers with a bias: the signed byte c becomes the fp16
+// value 1024 + (c + 128) = kI8Bias + c, exactly.  With 0x64 as the high byte
+// the number lies in [1024, 2048), where fp16 steps by 1, and the low byte
+// c xor 0x80 is c + 128.  A byte permute builds two of them per instruction,
+// against three instructions (two conversions and a pack) for exact codes.
+// The scores start from -kI8Bias times the sum of the query terms, and the
+// value sums drop kI8Bias times the weights they took (HeadState::vb).
+constexpr float kI8Bias = 1152.0f;
+constexpr uint32_t kBiasHigh = 0x64646464u;
+constexpr uint32_t kSignBits = 0x80808080u;
+
+// Codes 2i and 2i + 1 of word w (already xor kSignBits) as a biased pair.
+__device__ __forceinline__ uint32_t biased_pair(uint32_t u, int i) {
+  return __builtin_amdgcn_perm(kBiasHigh, u, i == 0 ? 0x04010400u : 0x04030402u);
+}
+// Code i of words w0 (low half) and w1 (high half) as a biased pair: the
+// permute puts the two bytes under zero high bytes, the xor flips their sign
+// bits and sets the high bytes to 0x64.
+__device__ __forceinline__ uint32_t biased_tokens(uint32_t w0, uint32_t w1, int i) {
+  const uint32_t sel = 0x0c000c00u | static_cast<uint32_t>(4 + i) << 16 | static_cast<uint32_t>(i);
+  return __builtin_amdgcn_perm(w1, w0, sel) ^ 0x64806480u;
+}
+
+// Takes the INT8 value bias out of the accumulators (kept below ~64 blocks
+// of weights, so the fp32 sums keep their precision).
+template <int HPW, int DPL>
+__device__ __forceinline__ void unbias(HeadState<HPW, DPL>& st) {
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) st.acc[h][e] = fmaf(-kI8Bias, st.vb[h], st.acc[h][e]);
+    st.vb[h] = 0.f;
   }
 }
 
@@ -109,7 +146,8 @@ struct Frag {
 // scaled query; bf16's 8 would cost ~0.5% in the scores).
 template <int KT, int D, int HPW>
 __device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b, int h0, int g,
-                                           uint32_t (&qv)[HPW][RowShape<KT, D>::QW]) {
+                                           uint32_t (&qv)[HPW][RowShape<KT, D>::QW],
+                                           float (&qb)[HPW]) {
   using S = RowShape<KT, D>;
   const int sub = lane & 7;
   if constexpr (KT == kI8) {
@@ -131,6 +169,15 @@ __device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b
           qv[h][2 * k + 1] = pack_f16x2(bf16_lo(q2[1]) * s4.z, bf16_hi(q2[1]) * s4.w);
         }
       }
+    // Start of each score: -kI8Bias times the lane's query terms, summed
+    // from the same fp16 values the products use.
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < S::QW; ++i) t = dot2_f16(qv[h][i], kF16OnePair, t);
+      qb[h] = -kI8Bias * t;
+    }
   } else {
     const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
                          (static_cast<size_t>(b) * a.num_q_heads + h0) * S::RW;
@@ -197,8 +244,8 @@ __device__ __forceinline__ void load_block(Frag<KT, D>& f, const PagedLaunch& a,
 template <int KT, int D, int HPW>
 __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
                                               const uint32_t (&qv)[HPW][RowShape<KT, D>::QW],
-                                              int lane, int nskip, int nvalid, float sl2,
-                                              HeadState<HPW, D / 8>& st) {
+                                              const float (&qb)[HPW], int lane, int nskip,
+                                              int nvalid, float sl2, HeadState<HPW, D / 8>& st) {
   using S = RowShape<KT, D>;
   constexpr int W = S::W, DPL = S::DPL;
   const int grp = lane >> 3;
@@ -206,33 +253,31 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
   float (&l)[HPW] = st.l;
   float (&acc)[HPW][DPL] = st.acc;
   float s[2][HPW];
-  // INT8: the codes widened to fp16 (exact), once for all heads: K as pairs
-  // of neighbouring dimensions, V as (token 0, token 1) pairs of one
-  // dimension.
+  // INT8: the codes as biased fp16 numbers (kI8Bias + code), once for all
+  // heads: K as pairs of neighbouring dimensions, V as (token 0, token 1)
+  // pairs of one dimension.
   uint32_t kp[KT == kI8 ? 2 : 1][KT == kI8 ? 2 * W : 1];
   uint32_t vp[KT == kI8 ? DPL : 1];
   if constexpr (KT == kI8) {
-    auto code = [](uint32_t word, int i) __attribute__((always_inline)) {
-      return static_cast<float>(static_cast<int8_t>(word >> (8 * i)));
-    };
 #pragma unroll
     for (int tok = 0; tok < 2; ++tok)
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        kp[tok][2 * w] = pack_f16x2_int(code(f.k[tok][w], 0), code(f.k[tok][w], 1));
-        kp[tok][2 * w + 1] = pack_f16x2_int(code(f.k[tok][w], 2), code(f.k[tok][w], 3));
+        const uint32_t u = f.k[tok][w] ^ kSignBits;
+        kp[tok][2 * w] = biased_pair(u, 0);
+        kp[tok][2 * w + 1] = biased_pair(u, 1);
       }
 #pragma unroll
     for (int w = 0; w < W; ++w)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vp[4 * w + i] = pack_f16x2_int(code(f.v[0][w], i), code(f.v[1][w], i));
+      for (int i = 0; i < 4; ++i) vp[4 * w + i] = biased_tokens(f.v[0][w], f.v[1][w], i);
   }
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok) {
     const bool ok = grp + 8 * tok >= nskip && grp + 8 * tok < nvalid;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-      float part = 0.f;
+      float part = KT == kI8 ? qb[h] : 0.f;
       if constexpr (KT == kI8) {
 #pragma unroll
         for (int i = 0; i < 2 * W; ++i) part = dot2_f16(qv[h][i], kp[tok][i], part);
@@ -259,6 +304,7 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
       const float mn = up ? mx : m[h];
       const float alpha = exp2_fast(m[h] - mn);
       l[h] *= alpha;
+      st.vb[h] *= alpha;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[h][e] *= alpha;
       m[h] = mn;
@@ -271,6 +317,7 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
       // plain weights, rounded the same way.
       l[h] = dot2_f16(pack_f16x2(p0, p1), kF16OnePair, l[h]);
       const uint32_t pp = pack_f16x2(p0 * f.vs[0], p1 * f.vs[1]);
+      st.vb[h] = dot2_f16(pp, kF16OnePair, st.vb[h]);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[h][e] = dot2_f16(pp, vp[e], acc[h][e]);
     } else {
@@ -343,7 +390,8 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
                                        HeadState<HPW, D / 8>& st, bool fused = false,
                                        bool write_new = false) {
   uint32_t qv[HPW][RowShape<KT, D>::QW];
-  load_query<KT, D, HPW>(a, lane, b, h0, g, qv);
+  float qb[HPW];
+  load_query<KT, D, HPW>(a, lane, b, h0, g, qv, qb);
   reset_state(st);
   const int t_last = t_end - 1;  // the appended position when fused
   if (fused) t_end = t_last;
@@ -377,15 +425,15 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
         if (jj < nblk) {
           int nv;
           block_of(jj, nv);
-          softmax_block<KT, D, HPW>(buf[s0], qv, lane,
-                                           max(0, t_start - (c0 + jj) * kBlockTokens), nv, sl2,
-                                           st);
+          softmax_block<KT, D, HPW>(buf[s0], qv, qb, lane,
+                                    max(0, t_start - (c0 + jj) * kBlockTokens), nv, sl2, st);
         }
         int nv;
         const int blk = block_of(jj + NBUF, nv);
         load_block<KT, D>(buf[s0], a, lane, g, blk, nv);
       }
     }
+    if constexpr (KT == kI8) unbias(st);
   }
   if (KT != kI8 && fused) {
     // The new rows, as token slot 0 of lane group 0 of a one-token block.
@@ -398,7 +446,7 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
       Frag<KT, D> f;
       load_rows<KT, D>(f, static_cast<const uint32_t*>(a.k_new) + src,
                          static_cast<const uint32_t*>(a.v_new) + src, a, lane, g, 1);
-      softmax_block<KT, D, HPW>(f, qv, lane, 0, 1, sl2, st);
+      softmax_block<KT, D, HPW>(f, qv, qb, lane, 0, 1, sl2, st);
       if (write_new && lane < 8) {
         const size_t dst = (static_cast<size_t>(blk) * kBlockTokens + t_last % kBlockTokens) * row_words +
                            g * S::RW;

@@ -17,7 +17,8 @@
  *   and launched", not "finished".  Calls on one stream run in order.
  * Errors: arguments are checked on the host before anything is launched; a
  *   negative status is returned and nothing is enqueued.  The checks read no
- *   device memory, so contents (seq_lens, table entries) are preconditions:
+ *   device memory (unless KVD_VALIDATE=1, below), so contents (seq_lens,
+ *   table entries) are preconditions:
  *     1 <= seq_lens[b] <= min(max_seq_len, max_blocks_per_seq * block_size);
  *     table entries of the blocks that hold positions < seq_lens[b] lie in
  *     [0, num_blocks); the block receiving an appended row is owned by that
@@ -28,6 +29,14 @@
  *   table entry outside [0, num_blocks) is skipped (its tokens contribute
  *   nothing and no append is made to it).  A sequence with seq_lens[b] <= 0
  *   gets an all-zero output row.
+ * KVD_VALIDATE=1 (environment variable, read at every call): each entry
+ *   point that launches kernels first copies its seq_lens, block table (and
+ *   cu_rows) and its small inputs (q, k_new, v_new) to the host, which
+ *   synchronises its stream, and returns KVD_ERR_SHAPE without launching
+ *   anything when one of the preconditions above fails (kvd_validate_tables,
+ *   kvd_validate_finite).  The cache contents are not scanned.  Meant for
+ *   debugging: it costs a round trip per call and must not be used under
+ *   HIP graph capture.
  * Layouts (row-major, innermost last):
  *   paged K or V cache   [num_blocks, block_size, num_kv_heads, head_dim]
  *       token-major inside a block, the per-token [seq, heads, d_head]
@@ -71,6 +80,37 @@ enum {
 
 /* Static English text for a status code (never NULL). */
 const char* kvd_status_string(int status);
+
+/*
+ * kvd_validate_tables -- the preconditions above, on HOST arrays (the checks
+ * KVD_VALIDATE=1 runs).
+ *   seq_lens     int32 [batch]; each must satisfy 1 <= seq_lens[b] <=
+ *                min(max_seq_len, max_blocks_per_seq * 16) (max_seq_len <= 0:
+ *                the table bound only)
+ *   block_table  int32 [batch, max_blocks_per_seq]; the entries of blocks
+ *                0 .. ceil(seq_lens[b] / 16) - 1 must lie in [0, num_blocks)
+ *   new_rows     NULL, or int32 [batch]: sequence b receives its last
+ *                new_rows[b] positions (0 <= new_rows[b] <= seq_lens[b]);
+ *                every block holding one of them must appear exactly once
+ *                among the visible entries of all sequences (owned, not
+ *                shared: the copy-on-write rule of "KV Cache（键值缓存）", 2.3
+ *                路线二)
+ *   first_bad    NULL, or receives the first offending sequence (-1 if none)
+ * Returns KVD_OK, KVD_ERR_SHAPE on a failed precondition, KVD_ERR_NULL for
+ * missing arrays.  Reads only the arrays given; allocates host memory for a
+ * per-block count when new_rows is given.
+ */
+int kvd_validate_tables(const int32_t* seq_lens, const int32_t* block_table, int batch,
+                        int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                        const int32_t* new_rows, int* first_bad);
+
+/*
+ * kvd_validate_finite -- KVD_OK when the `count` HOST values at `data`
+ * (bf16 or fp32 by dtype) are all finite, KVD_ERR_SHAPE when one is NaN or
+ * infinite (the single-step attention sketch of "KV缓存原理与显存估算", 知识点二,
+ * refuses non-finite inputs).
+ */
+int kvd_validate_finite(const void* data, size_t count, kvd_dtype_t dtype);
 
 /*
  * kv_append_paged -- write this step's K/V rows into their cache slots.

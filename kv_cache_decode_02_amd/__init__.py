@@ -36,6 +36,8 @@ from ._native import (
     block_hashes,
     BlockPool,
     PoolExhausted,
+    validate_tables,
+    validate_finite,
     LIB_PATH,
     HEADER_PATH,
 )
@@ -48,6 +50,6 @@ __all__ = [
     "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials", "mla_default_scale",
     "kv_append_paged_int8", "decode_attn_paged_int8", "decode_attn_paged_int8_partials",
     "kv_copy_blocks", "kv_append_paged_multi", "prefill_attn_paged", "block_hashes",
-    "BlockPool", "PoolExhausted",
+    "BlockPool", "PoolExhausted", "validate_tables", "validate_finite",
     "LIB_PATH", "HEADER_PATH",
 ]

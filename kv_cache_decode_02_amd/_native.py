@@ -103,6 +103,10 @@ lib.prefill_attn_paged.restype = _i
 lib.prefill_attn_paged.argtypes = [_vp] * 7 + [_i] * 9 + [_f, _i, _vp]
 lib.decode_attn_merge.restype = _i
 lib.decode_attn_merge.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _i, _vp]
+lib.kvd_validate_tables.restype = _i
+lib.kvd_validate_tables.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp]
+lib.kvd_validate_finite.restype = _i
+lib.kvd_validate_finite.argtypes = [_vp, _sz, _i]
 
 
 class KvdError(ValueError):
@@ -465,6 +469,34 @@ def decode_attn_paged_int8_partials(q, k_cache, v_cache, k_scale, v_scale, block
 
 
 # --- block copies and the host block pool ----------------------------------------
+
+def validate_tables(seq_lens, block_table, num_blocks, max_seq_len=0, new_rows=None):
+    """The library's host-side precondition check on host int32 arrays
+    (numpy or CPU tensors); returns None, raises KvdError naming the first
+    offending sequence."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens), dtype=np.int32)
+    table = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    if table.ndim != 2 or table.shape[0] != lens.shape[0]:
+        raise KvdError("validate_tables: block_table must be [batch, max_blocks_per_seq]")
+    rows = None if new_rows is None else np.ascontiguousarray(np.asarray(new_rows), dtype=np.int32)
+    bad = ctypes.c_int(-1)
+    st = lib.kvd_validate_tables(lens.ctypes.data, table.ctypes.data, lens.shape[0],
+                                 table.shape[1], num_blocks, max_seq_len,
+                                 None if rows is None else rows.ctypes.data, ctypes.byref(bad))
+    if st:
+        raise KvdError(f"validate_tables: {lib.kvd_status_string(st).decode()} "
+                       f"(status {st}, sequence {bad.value})")
+
+
+def validate_finite(values, dtype="bf16"):
+    """The library's host-side finiteness check: uint16 bf16 bit patterns or
+    float32 values in a host array; raises KvdError on NaN or infinity."""
+    import numpy as np
+    a = np.ascontiguousarray(values, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    code = KVD_BF16 if dtype == "bf16" else KVD_F32
+    _check(lib.kvd_validate_finite(a.ctypes.data, a.size, code), "validate_finite")
+
 
 def kv_copy_blocks(cache, pairs, stream=None):
     """Copy whole blocks of ``cache`` [num_blocks, ...]: block pairs[i, 0] onto

@@ -1,8 +1,13 @@
 // C ABI of the decode library: host-side argument checks, partition choice
 // and kernel dispatch.  Every check below runs before any HIP call, reads no
-// device memory and allocates nothing.
+// device memory and allocates nothing; with KVD_VALIDATE=1 the entry points
+// that launch kernels first also run the host-side precondition checks of
+// validate.cpp, which copy seq_lens, the block table and the small inputs to
+// the host (and so synchronise the stream).
 #include <limits.h>
 #include <stdint.h>
+
+#include <initializer_list>
 
 #include "../../include/kvdecode.h"
 #include "kvd_internal.h"
@@ -108,6 +113,31 @@ int check_table(int block_size, int max_blocks_per_seq, int num_blocks, int max_
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVD_OK : KVD_ERR_HIP; }
 
+// KVD_VALIDATE=1: the precondition checks of validate.cpp on this call's
+// device arrays; KVD_OK without touching the device otherwise.
+int preconditions(const int32_t* seq_lens, const int32_t* block_table, const int32_t* cu_rows,
+                  int batch, int max_blocks_per_seq, int num_blocks, int max_seq_len,
+                  bool writes_last, std::initializer_list<FiniteCheck> finite, void* stream) {
+  if (!validation_enabled()) return KVD_OK;
+  DeviceChecks c;
+  c.seq_lens = seq_lens;
+  c.block_table = block_table;
+  c.cu_rows = cu_rows;
+  c.batch = batch;
+  c.max_blocks_per_seq = max_blocks_per_seq;
+  c.num_blocks = num_blocks;
+  c.max_seq_len = max_seq_len;
+  c.writes_last = writes_last;
+  c.num_finite = 0;
+  for (const FiniteCheck& f : finite)
+    if (c.num_finite < 3 && f.ptr) c.finite[c.num_finite++] = f;
+  return validate_device(c, static_cast<hipStream_t>(stream));
+}
+
+size_t bytes_of(long long a, long long b, long long c, int dtype) {
+  return static_cast<size_t>(a * b * c * elem_bytes(dtype));
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -171,6 +201,11 @@ int kv_append_paged(void* k_cache, void* v_cache, const void* k_new, const void*
   a.num_blocks = num_blocks;
   a.vec16 = aligned16(k_cache) && aligned16(k_new) &&
             (!v_cache || (aligned16(v_cache) && aligned16(v_new)));
+  const size_t nb = static_cast<size_t>(batch) * static_cast<size_t>(row_bytes);
+  const int rc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
+                               num_blocks, 0, true, {{k_new, nb, dtype}, {v_new, nb, dtype}},
+                               stream);
+  if (rc) return rc;
   return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -283,6 +318,10 @@ int decode_attn_paged_partials(const void* q, const void* k_cache, const void* v
                              max_seq_len, partition_tokens, workspace, workspace_bytes, dtype, &s);
   if (rc) return rc;
   if (batch == 0) return KVD_OK;
+  const int vc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
+                               num_blocks, max_seq_len, false,
+                               {{q, bytes_of(batch, num_q_heads, head_dim, dtype), dtype}}, stream);
+  if (vc) return vc;
   const PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch,
                                      num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                                      num_blocks, max_seq_len, scale, workspace, dtype, s);
@@ -320,6 +359,10 @@ int decode_attn_paged(void* out, const void* q, const void* k_cache, const void*
   if (rc) return rc;
   if (batch == 0) return KVD_OK;
   if (!out) return KVD_ERR_NULL;
+  rc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq, num_blocks,
+                     max_seq_len, false,
+                     {{q, bytes_of(batch, num_q_heads, head_dim, dtype), dtype}}, stream);
+  if (rc) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch,
                                      num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
@@ -345,6 +388,10 @@ int decode_attn_paged_window_partials(const void* q, const void* k_cache, const 
   if (rc) return rc;
   if (window < 1) return KVD_ERR_SHAPE;
   if (batch == 0) return KVD_OK;
+  const int vc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
+                               num_blocks, max_seq_len, false,
+                               {{q, bytes_of(batch, num_q_heads, head_dim, dtype), dtype}}, stream);
+  if (vc) return vc;
   PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
                                num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                                max_seq_len, scale, workspace, dtype, s);
@@ -393,6 +440,14 @@ int decode_attn_paged_append_partials(const void* q, void* k_cache, void* v_cach
   if (batch == 0) return KVD_OK;
   if (!k_new || !v_new) return KVD_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVD_ERR_SHAPE;
+  const size_t nb = bytes_of(batch, num_kv_heads, head_dim, dtype);
+  const int vc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
+                               num_blocks, max_seq_len, true,
+                               {{q, bytes_of(batch, num_q_heads, head_dim, dtype), dtype},
+                                {k_new, nb, dtype},
+                                {v_new, nb, dtype}},
+                               stream);
+  if (vc) return vc;
   PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
                                num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                                max_seq_len, scale, workspace, dtype, s);
@@ -457,6 +512,11 @@ int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.bf16 = dtype == KVD_BF16;
+  const size_t nb = bytes_of(batch, num_kv_heads, head_dim, dtype);
+  const int rc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
+                               num_blocks, 0, true, {{k_new, nb, dtype}, {v_new, nb, dtype}},
+                               stream);
+  if (rc) return rc;
   return hip_status(launch_append_int8(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -493,6 +553,10 @@ int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const 
                                   max_blocks_per_seq, num_blocks, max_seq_len, partition_tokens,
                                   workspace, workspace_bytes, dtype, &s);
   if (rc || batch == 0) return rc;
+  const int vc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
+                               num_blocks, max_seq_len, false,
+                               {{q, bytes_of(batch, num_q_heads, head_dim, dtype), dtype}}, stream);
+  if (vc) return vc;
   PagedLaunch a = paged_launch(q, k_cache, v_cache, block_table, seq_lens, batch, num_q_heads,
                                num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                                max_seq_len, scale, workspace, dtype, s);
@@ -574,6 +638,9 @@ int kv_append_paged_multi(void* k_cache, void* v_cache, const void* k_new, const
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.vec16 = aligned16(k_cache) && aligned16(v_cache) && aligned16(k_new) && aligned16(v_new);
+  const int rc = preconditions(seq_lens, block_table, cu_rows, batch, max_blocks_per_seq,
+                               num_blocks, 0, false, {}, stream);
+  if (rc) return rc;
   return hip_status(launch_append_multi(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -598,6 +665,9 @@ int prefill_attn_paged(void* out, const void* q, const void* k_cache, const void
     return KVD_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return KVD_ERR_SHAPE;
+  rc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq, num_blocks,
+                     max_seq_len, false, {}, stream);
+  if (rc) return rc;
   PrefillLaunch a;
   a.q = q;
   a.k_cache = k_cache;
@@ -665,6 +735,11 @@ int decode_attn_mla_partials(const void* q, const void* c_cache,
                            block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale,
                            partition_tokens, workspace, workspace_bytes, &s, &a);
   if (rc || batch == 0) return rc;
+  const int vc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
+                               num_blocks, max_seq_len, false,
+                               {{q, bytes_of(batch, num_q_heads, d_c + d_rope, KVD_BF16), KVD_BF16}},
+                               stream);
+  if (vc) return vc;
   return hip_status(launch_mla_partials(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -681,6 +756,10 @@ int decode_attn_mla(void* out, const void* q, const void* c_cache,
                      partition_tokens, workspace, workspace_bytes, &s, &a);
   if (rc || batch == 0) return rc;
   if (!out) return KVD_ERR_NULL;
+  rc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq, num_blocks,
+                     max_seq_len, false,
+                     {{q, bytes_of(batch, num_q_heads, d_c + d_rope, KVD_BF16), KVD_BF16}}, stream);
+  if (rc) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   rc = hip_status(launch_mla_partials(a, st));
   if (rc) return rc;

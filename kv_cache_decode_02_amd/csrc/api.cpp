@@ -11,6 +11,7 @@
 
 #include "../../include/kvdecode.h"
 #include "kvd_internal.h"
+#include "kvd_validate.h"
 
 namespace kvd {
 

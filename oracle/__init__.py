@@ -21,6 +21,7 @@ Modules:
              partials + LSE merge, absorbed MLA, full causal recompute
   capacity   KV byte accounting (per token, useful / padded / paged, shared)
   quant      INT8 cache: per-channel K / per-token V codes, append, decode
+  quant_fp8  FP8 (E4M3) cache: the same scales over E4M3 codes
   allocator  block pool model: counts, fork, copy-on-write, chained keys
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against values
@@ -54,6 +55,15 @@ from .quant import (
     decode_attn_paged_int8,
     history_int8,
 )
+from .quant_fp8 import (
+    e4m3_value,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_fp8,
+    channel_scales_fp8,
+    append_paged_fp8,
+    decode_attn_paged_fp8,
+)
 from .allocator import block_hashes, BlockPool, PoolExhausted
 from .capacity import (
     bytes_per_token,
@@ -74,5 +84,7 @@ __all__ = [
     "kv_cache_bytes", "mla_elements_per_token",
     "quantize", "token_scale", "channel_scales", "append_paged_int8", "dequantize_k",
     "dequantize_v", "decode_attn_paged_int8", "history_int8",
+    "e4m3_value", "e4m3_decode", "e4m3_encode", "quantize_fp8", "channel_scales_fp8",
+    "append_paged_fp8", "decode_attn_paged_fp8",
     "block_hashes", "BlockPool", "PoolExhausted",
 ]

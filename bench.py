@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_llama3_8b",
                     choices=["gqa_llama3_8b", "mha_llama2_7b", "long_gqa_split", "tiny",
-                             "mla_deepseek_v2", "gqa_llama3_8b_int8", "prefill_llama3_8b"])
+                             "mla_deepseek_v2", "gqa_llama3_8b_int8", "gqa_llama3_8b_fp8",
+                             "prefill_llama3_8b"])
     ap.add_argument("--replicas", type=int, default=4,
                     help="MLA: rotate over this many copies of the latent cache so the "
                          "timed reads come from HBM, not the 256 MB Infinity Cache")
@@ -237,8 +238,8 @@ def cpu_baseline_mla(inp, target_s, scale):
 
 
 def cpu_baseline_int8(inp, target_s):
-    """Time the fp64 oracle (quantising append + INT8 decode) on whole
-    sequences of the INT8 workload until ~target_s."""
+    """Time the fp64 oracle (quantising append + decode over the one-byte
+    cache, INT8 or FP8) on whole sequences of the workload until ~target_s."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -255,11 +256,13 @@ def cpu_baseline_int8(inp, target_s):
         # the sequence's own blocks, appended to and read as one small pool
         blocks = inp.block_table[b, :-(-n // 16)]
         table = np.arange(len(blocks), dtype=np.int32)[None, :]
-        kq, vq, vs = oracle.append_paged_int8(inp.kq_pool[blocks], inp.vq_pool[blocks],
-                                              inp.vs_pool[blocks], inp.k_new[sl], inp.v_new[sl],
-                                              "bf16", inp.k_scale, table, inp.seq_lens[sl])
-        oracle.decode_attn_paged_int8(inp.q[sl], kq, vq, vs, inp.k_scale, table,
-                                      inp.seq_lens[sl], "bf16")
+        fp8 = inp.codes == "fp8"
+        append = oracle.append_paged_fp8 if fp8 else oracle.append_paged_int8
+        decode = oracle.decode_attn_paged_fp8 if fp8 else oracle.decode_attn_paged_int8
+        kq, vq, vs = append(inp.kq_pool[blocks], inp.vq_pool[blocks], inp.vs_pool[blocks],
+                            inp.k_new[sl], inp.v_new[sl], "bf16", inp.k_scale, table,
+                            inp.seq_lens[sl])
+        decode(inp.q[sl], kq, vq, vs, inp.k_scale, table, inp.seq_lens[sl], "bf16")
         done += 1
         tokens += n
     dt = time.perf_counter() - t0
@@ -272,8 +275,9 @@ def cpu_baseline_int8(inp, target_s):
 
 
 def main_int8(args, kvd, make_config_inputs):
-    """One decode step over the INT8 cache: the quantising append, the partial
-    kernel and the merge, timed like the bf16 step (graph replay)."""
+    """One decode step over a one-byte cache (INT8 or FP8 E4M3 codes): the
+    quantising append, the partial kernel and the merge, timed like the bf16
+    step (graph replay)."""
     import torch
     dev = torch.device("cuda:0")
     inp = make_config_inputs(args.workload, sentinel="zero")[0]
@@ -288,12 +292,15 @@ def main_int8(args, kvd, make_config_inputs):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
+    fp8 = inp.codes == "fp8"
+    append = kvd.kv_append_paged_fp8 if fp8 else kvd.kv_append_paged_int8
+    partials = kvd.decode_attn_paged_fp8_partials if fp8 else kvd.decode_attn_paged_int8_partials
+
     def step(ev=None):
-        kvd.kv_append_paged_int8(kq, vq, vs, kn, vn, ks, table, seq)
+        append(kq, vq, vs, kn, vn, ks, table, seq)
         if ev is not None:
             ev[0].record(stream)
-        kvd.decode_attn_paged_int8_partials(q, kq, vq, ks, vs, table, seq, L, ws,
-                                            partition_tokens=pt)
+        partials(q, kq, vq, ks, vs, table, seq, L, ws, partition_tokens=pt)
         if ev is not None:
             ev[1].record(stream)
         kvd.decode_attn_merge(out, seq, H_kv, L, ws, partition_tokens=pt)
@@ -325,15 +332,17 @@ def main_int8(args, kvd, make_config_inputs):
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3" if fp8 else "int8",
         "step_launch": "hip graph" if not args.no_graph else "eager",
-        "step_kernels": "kv_append_paged_int8, partials, merge",
+        "step_kernels": f"kv_append_paged_{'fp8' if fp8 else 'int8'}, partials, merge",
         "ms_per_step_eager": round(ms_eager, 5), "graph_replays_match_eager": graph_check,
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": H_q,
                    "num_kv_heads": H_kv, "head_dim": d, "block_size": 16,
                    "sum_seq_len": int(inp.seq_lens.astype(np.int64).sum()), "max_seq_len": L,
-                   "partition_tokens": pt_used, "cache": "int8 codes, per-channel K and "
+                   "partition_tokens": pt_used,
+                   "cache": f"{'fp8 e4m3' if fp8 else 'int8'} codes, per-channel K and "
                    "per-token V fp32 scales; bf16 queries and output"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(inp.B / (ms_step / 1e3), 1),
@@ -573,7 +582,7 @@ def main():
     if cfg["kind"] == "mla":
         main_mla(args, kvd, make_config_inputs)
         return
-    if cfg["kind"] == "paged_int8":
+    if cfg["kind"] in ("paged_int8", "paged_fp8"):
         main_int8(args, kvd, make_config_inputs)
         return
     if cfg["kind"] == "prefill":

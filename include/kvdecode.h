@@ -400,6 +400,47 @@ int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const 
                                     void* stream);
 
 /*
+ * FP8 cache ("KV-Cache——为什么AI回复越来越快", KV-Cache量化: FP16 K/V stored
+ * in FP8, one byte, with per-channel K and per-token V scales).  The same
+ * layouts, scales and calls as the INT8 cache above, with E4M3 codes in place
+ * of integers: the OCP 8-bit floating-point E4M3 format (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 =
+ * NaN, largest finite 448).
+ *   append: code = E4M3(x / s) with the correctly rounded fp32 quotient, the
+ *     nearest E4M3 value, ties to the even code, magnitudes beyond 448
+ *     saturating to 448 (no NaN codes are written) and the quotient's sign
+ *     bit kept (-0 for a negative quotient that rounds to zero); V's scale is
+ *     max |v| / 448 of its own row (0 and all codes 0 for a zero row).
+ *   decode: a stored value is E4M3(code) * scale.
+ *   k_cache, v_cache  uint8 [num_blocks, 16, num_kv_heads, head_dim] codes
+ * Other arguments, sizes, alignment and errors as for the INT8 functions.
+ */
+int kv_append_paged_fp8(uint8_t* k_cache, uint8_t* v_cache, float* v_scale, const void* k_new,
+                        const void* v_new, const float* k_scale, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,
+                        int block_size, int max_blocks_per_seq, int num_blocks,
+                        kvd_dtype_t dtype, void* stream);
+
+int decode_attn_paged_fp8(void* out, const void* q, const uint8_t* k_cache,
+                          const uint8_t* v_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, int batch,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                          int partition_tokens, void* workspace, size_t workspace_bytes,
+                          kvd_dtype_t dtype, void* stream);
+
+/* decode_attn_paged_fp8_partials -- first phase of decode_attn_paged_fp8
+ * (finish with decode_attn_merge, dtype KVD_BF16). */
+int decode_attn_paged_fp8_partials(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int max_blocks_per_seq, int num_blocks,
+                                   int max_seq_len, float scale, int partition_tokens,
+                                   void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                                   void* stream);
+
+/*
  * Chunked prefill and multi-token decode ("单请求 KV Cache", 改动三: a row at
  * position past_len + i sees mask[i, :past_len + i + 1], the prefill triangle
  * for past_len = 0 and the decode row for one new token; "KV缓存原理与显存估算",

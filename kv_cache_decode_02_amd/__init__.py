@@ -5,7 +5,7 @@ into the paged cache, ``decode_attn_paged`` attends over the whole visible
 history (split-KV partials, then a log-sum-exp merge), and
 ``decode_attn_paged_append`` does both in one pass; ``kv_append_paged_int8``
 and ``decode_attn_paged_int8`` are the same step over an INT8 cache (K scaled
-per channel, V per token); ``decode_attn_mla`` is the absorbed multi-head
+per channel, V per token), the ``_fp8`` functions over an FP8 (E4M3) cache; ``decode_attn_mla`` is the absorbed multi-head
 latent attention variant over a latent cache.  The functions mirror
 the C ABI in ``include/kvdecode.h`` and only marshal arguments; importing this
 package fails if the HIP library has not been built.
@@ -30,6 +30,9 @@ from ._native import (
     kv_append_paged_int8,
     decode_attn_paged_int8,
     decode_attn_paged_int8_partials,
+    kv_append_paged_fp8,
+    decode_attn_paged_fp8,
+    decode_attn_paged_fp8_partials,
     kv_copy_blocks,
     kv_append_paged_multi,
     prefill_attn_paged,
@@ -49,6 +52,7 @@ __all__ = [
     "decode_attn_merge", "decode_attn_workspace_bytes", "decode_attn_partition_tokens",
     "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials", "mla_default_scale",
     "kv_append_paged_int8", "decode_attn_paged_int8", "decode_attn_paged_int8_partials",
+    "kv_append_paged_fp8", "decode_attn_paged_fp8", "decode_attn_paged_fp8_partials",
     "kv_copy_blocks", "kv_append_paged_multi", "prefill_attn_paged", "block_hashes",
     "BlockPool", "PoolExhausted", "validate_tables", "validate_finite",
     "LIB_PATH", "HEADER_PATH",

@@ -64,6 +64,12 @@ lib.decode_attn_paged_int8.restype = _i
 lib.decode_attn_paged_int8.argtypes = [_vp] + _INT8_ARGS
 lib.decode_attn_paged_int8_partials.restype = _i
 lib.decode_attn_paged_int8_partials.argtypes = _INT8_ARGS
+lib.kv_append_paged_fp8.restype = _i
+lib.kv_append_paged_fp8.argtypes = [_vp] * 8 + [_i] * 7 + [_vp]
+lib.decode_attn_paged_fp8.restype = _i
+lib.decode_attn_paged_fp8.argtypes = [_vp] + _INT8_ARGS
+lib.decode_attn_paged_fp8_partials.restype = _i
+lib.decode_attn_paged_fp8_partials.argtypes = _INT8_ARGS
 # the paged arguments with `window` after `scale`
 _WINDOW_ARGS = _PAGED_ARGS[:14] + [_i] + _PAGED_ARGS[14:]
 lib.decode_attn_paged_window.restype = _i
@@ -389,8 +395,22 @@ def kv_append_paged_int8(k_cache, v_cache, v_scale, k_new, v_new, k_scale, block
     k_cache/v_cache: int8 [num_blocks, 16, H_kv, d]; k_new/v_new: [B, H_kv, d]
     bf16 or fp32.
     """
-    _need(k_cache, "k_cache", dtype=torch.int8)
-    _need(v_cache, "v_cache", dtype=torch.int8)
+    _append_bytes("kv_append_paged_int8", torch.int8, k_cache, v_cache, v_scale, k_new, v_new,
+                  k_scale, block_table, seq_lens, stream)
+
+
+def kv_append_paged_fp8(k_cache, v_cache, v_scale, k_new, v_new, k_scale, block_table,
+                        seq_lens, stream=None):
+    """As kv_append_paged_int8 for an FP8 cache: uint8 E4M3 codes, V scale
+    max |v| / 448."""
+    _append_bytes("kv_append_paged_fp8", torch.uint8, k_cache, v_cache, v_scale, k_new, v_new,
+                  k_scale, block_table, seq_lens, stream)
+
+
+def _append_bytes(name, code_dtype, k_cache, v_cache, v_scale, k_new, v_new, k_scale,
+                  block_table, seq_lens, stream):
+    _need(k_cache, "k_cache", dtype=code_dtype)
+    _need(v_cache, "v_cache", dtype=code_dtype)
     _need(v_scale, "v_scale", dtype=torch.float32)
     _need(k_scale, "k_scale", dtype=torch.float32)
     _need(k_new, "k_new")
@@ -405,21 +425,21 @@ def kv_append_paged_int8(k_cache, v_cache, v_scale, k_new, v_new, k_scale, block
     B = k_new.shape[0]
     if tuple(k_new.shape) != (B, h_kv, d) or tuple(v_new.shape) != (B, h_kv, d):
         raise KvdError("k_new and v_new must be [B, H_kv, d]")
-    status = lib.kv_append_paged_int8(_ptr(k_cache), _ptr(v_cache), _ptr(v_scale), _ptr(k_new),
-                                      _ptr(v_new), _ptr(k_scale), _ptr(block_table),
-                                      _ptr(seq_lens), B, h_kv, d, bs, block_table.shape[1], nb,
-                                      _dtype_code(k_new), _stream(stream))
-    _check(status, "kv_append_paged_int8")
+    status = getattr(lib, name)(_ptr(k_cache), _ptr(v_cache), _ptr(v_scale), _ptr(k_new),
+                                _ptr(v_new), _ptr(k_scale), _ptr(block_table), _ptr(seq_lens), B,
+                                h_kv, d, bs, block_table.shape[1], nb, _dtype_code(k_new),
+                                _stream(stream))
+    _check(status, name)
 
 
 def _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len, scale,
-               partition_tokens, ws):
+               partition_tokens, ws, code_dtype=torch.int8):
     for t, n in ((q, "q"), (block_table, "block_table"), (seq_lens, "seq_lens"),
                  (ws, "workspace")):
         _need(t, n)
     _need(q, "q", dtype=torch.bfloat16)
-    _need(k_cache, "k_cache", dtype=torch.int8)
-    _need(v_cache, "v_cache", dtype=torch.int8)
+    _need(k_cache, "k_cache", dtype=code_dtype)
+    _need(v_cache, "v_cache", dtype=code_dtype)
     _need(k_scale, "k_scale", dtype=torch.float32)
     _need(v_scale, "v_scale", dtype=torch.float32)
     _need(block_table, "block_table", dtype=torch.int32)
@@ -466,6 +486,35 @@ def decode_attn_paged_int8_partials(q, k_cache, v_cache, k_scale, v_scale, block
                       scale, partition_tokens, workspace)
     _check(lib.decode_attn_paged_int8_partials(*args, _stream(stream)),
            "decode_attn_paged_int8_partials")
+
+
+def decode_attn_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
+                          max_seq_len, scale=None, partition_tokens=0, workspace=None, out=None,
+                          stream=None):
+    """Decode attention of bf16 q [B, H_q, d] over an FP8 (E4M3, uint8 codes)
+    paged cache; returns the bf16 output."""
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    if workspace is None:
+        workspace = alloc_workspace(B, h_q, h_kv, d, max_seq_len, partition_tokens,
+                                    device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=torch.bfloat16)
+    args = _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                      scale, partition_tokens, workspace, code_dtype=torch.uint8)
+    _check(lib.decode_attn_paged_fp8(_ptr(out), *args, _stream(stream)), "decode_attn_paged_fp8")
+    return out
+
+
+def decode_attn_paged_fp8_partials(q, k_cache, v_cache, k_scale, v_scale, block_table,
+                                   seq_lens, max_seq_len, workspace, scale=None,
+                                   partition_tokens=0, stream=None):
+    """First phase of decode_attn_paged_fp8 only; finish with decode_attn_merge."""
+    args = _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                      scale, partition_tokens, workspace, code_dtype=torch.uint8)
+    _check(lib.decode_attn_paged_fp8_partials(*args, _stream(stream)),
+           "decode_attn_paged_fp8_partials")
 
 
 # --- block copies and the host block pool ----------------------------------------

@@ -279,6 +279,7 @@ static PagedLaunch paged_launch(const void* q, const void* k_cache, const void* 
   a.k_new = nullptr;
   a.v_new = nullptr;
   a.int8 = false;
+  a.fp8 = false;
   a.k_scale = nullptr;
   a.v_scale = nullptr;
   a.window = 0;
@@ -483,11 +484,11 @@ int decode_attn_paged_append(void* out, const void* q, void* k_cache, void* v_ca
                            partition_tokens, workspace, workspace_bytes, dtype, stream);
 }
 
-int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const void* k_new,
-                         const void* v_new, const float* k_scale, const int32_t* block_table,
-                         const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,
-                         int block_size, int max_blocks_per_seq, int num_blocks,
-                         kvd_dtype_t dtype, void* stream) {
+static int append_bytes(void* k_cache, void* v_cache, float* v_scale, const void* k_new,
+                        const void* v_new, const float* k_scale, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,
+                        int block_size, int max_blocks_per_seq, int num_blocks, int dtype,
+                        bool fp8, void* stream) {
   if (!dtype_ok(dtype)) return KVD_ERR_UNSUPPORTED;
   if (batch < 0 || num_kv_heads < 1) return KVD_ERR_SHAPE;
   if (!(head_dim == 32 || head_dim == 64 || head_dim == 128)) return KVD_ERR_UNSUPPORTED;
@@ -499,8 +500,8 @@ int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const
       !seq_lens)
     return KVD_ERR_NULL;
   AppendInt8Launch a;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  a.k_cache = static_cast<int8_t*>(k_cache);
+  a.v_cache = static_cast<int8_t*>(v_cache);
   a.v_scale = v_scale;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -513,12 +514,33 @@ int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.bf16 = dtype == KVD_BF16;
+  a.fp8 = fp8;
   const size_t nb = bytes_of(batch, num_kv_heads, head_dim, dtype);
   const int rc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq,
                                num_blocks, 0, true, {{k_new, nb, dtype}, {v_new, nb, dtype}},
                                stream);
   if (rc) return rc;
   return hip_status(launch_append_int8(a, static_cast<hipStream_t>(stream)));
+}
+
+int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const void* k_new,
+                         const void* v_new, const float* k_scale, const int32_t* block_table,
+                         const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int num_blocks,
+                         kvd_dtype_t dtype, void* stream) {
+  return append_bytes(k_cache, v_cache, v_scale, k_new, v_new, k_scale, block_table, seq_lens,
+                      batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                      dtype, false, stream);
+}
+
+int kv_append_paged_fp8(uint8_t* k_cache, uint8_t* v_cache, float* v_scale, const void* k_new,
+                        const void* v_new, const float* k_scale, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,
+                        int block_size, int max_blocks_per_seq, int num_blocks,
+                        kvd_dtype_t dtype, void* stream) {
+  return append_bytes(k_cache, v_cache, v_scale, k_new, v_new, k_scale, block_table, seq_lens,
+                      batch, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                      dtype, true, stream);
 }
 
 // The INT8 decode takes bf16 queries (and writes a bf16 output); its scales
@@ -540,14 +562,13 @@ static int check_paged_int8(const void* q, const void* k_cache, const void* v_ca
   return KVD_OK;
 }
 
-int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const int8_t* v_cache,
-                                    const float* k_scale, const float* v_scale,
-                                    const int32_t* block_table, const int32_t* seq_lens,
-                                    int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                                    int block_size, int max_blocks_per_seq, int num_blocks,
-                                    int max_seq_len, float scale, int partition_tokens,
-                                    void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
-                                    void* stream) {
+static int bytes_partials(const void* q, const void* k_cache, const void* v_cache,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, int batch,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                          int partition_tokens, void* workspace, size_t workspace_bytes,
+                          int dtype, bool fp8, void* stream) {
   Sizes s;
   const int rc = check_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
                                   batch, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -562,9 +583,62 @@ int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const 
                                num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                                max_seq_len, scale, workspace, dtype, s);
   a.int8 = true;
+  a.fp8 = fp8;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   return hip_status(launch_paged_partials(a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_paged_int8_partials(const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                    int block_size, int max_blocks_per_seq, int num_blocks,
+                                    int max_seq_len, float scale, int partition_tokens,
+                                    void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                                    void* stream) {
+  return bytes_partials(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, max_seq_len, scale, partition_tokens, workspace,
+                        workspace_bytes, dtype, false, stream);
+}
+
+int decode_attn_paged_fp8_partials(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int block_size, int max_blocks_per_seq, int num_blocks,
+                                   int max_seq_len, float scale, int partition_tokens,
+                                   void* workspace, size_t workspace_bytes, kvd_dtype_t dtype,
+                                   void* stream) {
+  return bytes_partials(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
+                        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, max_seq_len, scale, partition_tokens, workspace,
+                        workspace_bytes, dtype, true, stream);
+}
+
+static int bytes_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens, int batch,
+                        int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                        int partition_tokens, void* workspace, size_t workspace_bytes, int dtype,
+                        bool fp8, void* stream) {
+  Sizes s;
+  int rc = check_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
+                            num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                            num_blocks, max_seq_len, partition_tokens, workspace,
+                            workspace_bytes, dtype, &s);
+  if (rc || batch == 0) return rc;
+  if (!out) return KVD_ERR_NULL;
+  rc = bytes_partials(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
+                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                      num_blocks, max_seq_len, scale, partition_tokens, workspace,
+                      workspace_bytes, dtype, fp8, stream);
+  if (rc) return rc;
+  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
+                                     workspace, dtype, s);
+  return hip_status(launch_merge(m, static_cast<hipStream_t>(stream)));
 }
 
 int decode_attn_paged_int8(void* out, const void* q, const int8_t* k_cache, const int8_t* v_cache,
@@ -574,22 +648,23 @@ int decode_attn_paged_int8(void* out, const void* q, const int8_t* k_cache, cons
                            int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
                            int partition_tokens, void* workspace, size_t workspace_bytes,
                            kvd_dtype_t dtype, void* stream) {
-  Sizes s;
-  int rc = check_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
-                            num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                            num_blocks, max_seq_len, partition_tokens, workspace,
-                            workspace_bytes, dtype, &s);
-  if (rc || batch == 0) return rc;
-  if (!out) return KVD_ERR_NULL;
-  rc = decode_attn_paged_int8_partials(q, k_cache, v_cache, k_scale, v_scale, block_table,
-                                       seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
-                                       block_size, max_blocks_per_seq, num_blocks, max_seq_len,
-                                       scale, partition_tokens, workspace, workspace_bytes,
-                                       dtype, stream);
-  if (rc) return rc;
-  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, head_dim, max_seq_len,
-                                     workspace, dtype, s);
-  return hip_status(launch_merge(m, static_cast<hipStream_t>(stream)));
+  return bytes_decode(out, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
+                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                      num_blocks, max_seq_len, scale, partition_tokens, workspace,
+                      workspace_bytes, dtype, false, stream);
+}
+
+int decode_attn_paged_fp8(void* out, const void* q, const uint8_t* k_cache,
+                          const uint8_t* v_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, int batch,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                          int partition_tokens, void* workspace, size_t workspace_bytes,
+                          kvd_dtype_t dtype, void* stream) {
+  return bytes_decode(out, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, batch,
+                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                      num_blocks, max_seq_len, scale, partition_tokens, workspace,
+                      workspace_bytes, dtype, true, stream);
 }
 
 int kv_copy_blocks(void* cache, const int32_t* pairs, int num_pairs, size_t block_bytes,

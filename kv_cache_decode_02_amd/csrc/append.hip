@@ -50,7 +50,41 @@ __device__ __forceinline__ int8_t quantize_code(float x, float s) {
   return static_cast<int8_t>(fminf(fmaxf(r, -127.f), 127.f));
 }
 
-template <bool BF16, int D>
+// FP8 cache: the E4M3 byte (OCP 8-bit float: bias 7, 3 mantissa bits,
+// subnormals, largest finite 448) nearest to y, ties to the even code,
+// magnitudes past 448 saturating, with y's sign bit.  Subnormal range
+// (|y| < 2^-6): the count of 2^-9 steps, rint(|y| * 512) (exact scaling,
+// round half to even), whose codes 0 .. 8 run on into the normal ones.
+// Normal range: |y|'s fp32 pattern rounded to 3 mantissa bits, half to
+// even, then re-biased from 127 to 7 (the carry of a round-up moves into
+// the exponent, as the E4M3 pattern needs).
+__device__ __forceinline__ uint8_t e4m3_code(float y) {
+  const uint32_t bits = __float_as_uint(y);
+  const float a = fabsf(y);
+  uint32_t mag;
+  if (a >= 448.f) {
+    mag = 0x7E;
+  } else if (a < 0.015625f) {
+    mag = static_cast<uint32_t>(rintf(a * 512.f));
+  } else {
+    const uint32_t u = bits & 0x7FFFFFFFu;
+    const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    mag = (r >> 20) - (120u << 3);
+  }
+  return static_cast<uint8_t>(mag | ((bits >> 24) & 0x80u));
+}
+
+template <bool FP8>
+__device__ __forceinline__ int8_t quantize_byte(float x, float s) {
+  if constexpr (FP8) {
+    if (!(s > 0.f)) return 0;
+    return static_cast<int8_t>(e4m3_code(__fdiv_rn(x, s)));
+  } else {
+    return quantize_code(x, s);
+  }
+}
+
+template <bool BF16, int D, bool FP8>
 __global__ __launch_bounds__(256) void append_int8_kernel(AppendInt8Launch a) {
   constexpr int EPL = (D + kWave - 1) / kWave;  // elements per lane
   const int b = blockIdx.x;
@@ -85,26 +119,26 @@ __global__ __launch_bounds__(256) void append_int8_kernel(AppendInt8Launch a) {
     }
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) vmax = fmaxf(vmax, shfl_xor_f(vmax, sh));
-    const float vs = __fdiv_rn(vmax, 127.f);
+    const float vs = __fdiv_rn(vmax, FP8 ? 448.f : 127.f);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int j = lane + i * kWave;
       if (j < D) {
-        a.k_cache[dst + j] = quantize_code(kx[i], a.k_scale[static_cast<size_t>(g) * D + j]);
-        a.v_cache[dst + j] = quantize_code(vx[i], vs);
+        a.k_cache[dst + j] = quantize_byte<FP8>(kx[i], a.k_scale[static_cast<size_t>(g) * D + j]);
+        a.v_cache[dst + j] = quantize_byte<FP8>(vx[i], vs);
       }
     }
     if (lane == 0) a.v_scale[row * a.num_kv_heads + g] = vs;
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool FP8>
 hipError_t launch_append_int8_typed(const AppendInt8Launch& a, hipStream_t stream) {
   const dim3 grid(a.batch), block(256);
   switch (a.head_dim) {
-    case 32: hipLaunchKernelGGL((append_int8_kernel<BF16, 32>), grid, block, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL((append_int8_kernel<BF16, 64>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((append_int8_kernel<BF16, 128>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((append_int8_kernel<BF16, 32, FP8>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((append_int8_kernel<BF16, 64, FP8>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((append_int8_kernel<BF16, 128, FP8>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }
@@ -173,7 +207,11 @@ hipError_t launch_copy_blocks(const CopyBlocksLaunch& a, hipStream_t stream) {
 }
 
 hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream) {
-  return a.bf16 ? launch_append_int8_typed<true>(a, stream) : launch_append_int8_typed<false>(a, stream);
+  if (a.fp8)
+    return a.bf16 ? launch_append_int8_typed<true, true>(a, stream)
+                  : launch_append_int8_typed<false, true>(a, stream);
+  return a.bf16 ? launch_append_int8_typed<true, false>(a, stream)
+                : launch_append_int8_typed<false, false>(a, stream);
 }
 
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream) {

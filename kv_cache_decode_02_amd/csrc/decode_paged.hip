@@ -36,9 +36,9 @@
 namespace kvd {
 namespace {
 
-// Storage of the K/V cache: fp32, bf16, or INT8 codes with per-channel K and
-// per-token V scales.
-enum Kind : int { kF32 = 0, kBF16 = 1, kI8 = 2 };
+// Storage of the K/V cache: fp32, bf16, or one-byte codes (INT8 or FP8 E4M3)
+// with per-channel K and per-token V scales.
+enum Kind : int { kF32 = 0, kBF16 = 1, kI8 = 2, kF8 = 3 };
 
 constexpr float kRaise = 8.0f;
 constexpr int kMaxPartitionBlocks = 64;  // one block id per lane
@@ -64,7 +64,7 @@ struct RowShape {
   static constexpr int RW = D / EPW;        // words per row (one head)
   // Query words per lane: INT8 codes are widened to bf16 pairs, so each code
   // word meets two words of (scaled) query.
-  static constexpr int QW = KT == kI8 ? 2 * W : W;
+  static constexpr int QW = KT >= kI8 ? 2 * W : W;
   static_assert(W >= 1 && W % CW == 0, "unsupported head_dim");
   // Word offset, inside a row, of the lane's chunk c.
   static __device__ __forceinline__ int chunk_word(int c, int sub) { return (c * 8 + sub) * CW; }
@@ -136,7 +136,7 @@ template <int KT, int D>
 struct Frag {
   uint32_t k[2][RowShape<KT, D>::W];
   uint32_t v[2][RowShape<KT, D>::W];
-  float vs[KT == kI8 ? 2 : 1];
+  float vs[KT >= kI8 ? 2 : 1];
 };
 
 // Query slice of heads h0 .. h0 + HPW - 1 of sequence b, in the lane layout of
@@ -150,7 +150,7 @@ __device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b
                                            float (&qb)[HPW]) {
   using S = RowShape<KT, D>;
   const int sub = lane & 7;
-  if constexpr (KT == kI8) {
+  if constexpr (KT >= kI8) {
     const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
                          (static_cast<size_t>(b) * a.num_q_heads + h0) * (D / 2);
     const float* ks = a.k_scale + static_cast<size_t>(g) * D;
@@ -169,14 +169,15 @@ __device__ __forceinline__ void load_query(const PagedLaunch& a, int lane, int b
           qv[h][2 * k + 1] = pack_f16x2(bf16_lo(q2[1]) * s4.z, bf16_hi(q2[1]) * s4.w);
         }
       }
-    // Start of each score: -kI8Bias times the lane's query terms, summed
-    // from the same fp16 values the products use.
+    // INT8: each score starts from -kI8Bias times the lane's query terms,
+    // summed from the same fp16 values the products use.  (FP8 codes widen
+    // exactly, with no bias.)
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
       float t = 0.f;
 #pragma unroll
       for (int i = 0; i < S::QW; ++i) t = dot2_f16(qv[h][i], kF16OnePair, t);
-      qb[h] = -kI8Bias * t;
+      qb[h] = KT == kI8 ? -kI8Bias * t : 0.f;
     }
   } else {
     const uint32_t* qw = static_cast<const uint32_t*>(a.q) +
@@ -217,7 +218,7 @@ __device__ __forceinline__ void load_rows(Frag<KT, D>& f, const uint32_t* kbase,
       buffer_load_words<S::CW>(&f.v[tok][c * S::CW], rv, off + c * 8 * S::CW * 4);
     }
   }
-  if constexpr (KT == kI8) {
+  if constexpr (KT >= kI8) {
     // V scales [token][KV head] of the block, nvalid tokens.
     const BufRsrc rs = make_rsrc(sbase, nvalid * a.num_kv_heads * 4);
 #pragma unroll
@@ -236,7 +237,7 @@ __device__ __forceinline__ void load_block(Frag<KT, D>& f, const PagedLaunch& a,
   const size_t base = blk0 * tok_stride;
   load_rows<KT, D>(f, static_cast<const uint32_t*>(a.k_cache) + base,
                    static_cast<const uint32_t*>(a.v_cache) + base, a, lane, g, nvalid,
-                   KT == kI8 ? a.v_scale + blk0 * a.num_kv_heads : nullptr);
+                   KT >= kI8 ? a.v_scale + blk0 * a.num_kv_heads : nullptr);
 }
 
 // One block through the online softmax of HPW heads; tokens [nskip, nvalid)
@@ -253,11 +254,34 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
   float (&l)[HPW] = st.l;
   float (&acc)[HPW][DPL] = st.acc;
   float s[2][HPW];
-  // INT8: the codes as biased fp16 numbers (kI8Bias + code), once for all
-  // heads: K as pairs of neighbouring dimensions, V as (token 0, token 1)
-  // pairs of one dimension.
-  uint32_t kp[KT == kI8 ? 2 : 1][KT == kI8 ? 2 * W : 1];
-  uint32_t vp[KT == kI8 ? DPL : 1];
+  // One-byte codes as fp16 pairs, once for all heads: K as pairs of
+  // neighbouring dimensions, V as (token 0, token 1) pairs of one dimension.
+  // INT8: biased numbers kI8Bias + code (byte permutes).  FP8: the exact
+  // E4M3 values (v_cvt_pk_f32_fp8, then a pack that is exact since every
+  // E4M3 value is an fp16 number).
+  uint32_t kp[KT >= kI8 ? 2 : 1][KT >= kI8 ? 2 * W : 1];
+  uint32_t vp[KT >= kI8 ? DPL : 1];
+  if constexpr (KT == kF8) {
+#pragma unroll
+    for (int tok = 0; tok < 2; ++tok)
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(f.k[tok][w], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(f.k[tok][w], true);
+        kp[tok][2 * w] = pack_f16x2_int(lo[0], lo[1]);
+        kp[tok][2 * w + 1] = pack_f16x2_int(hi[0], hi[1]);
+      }
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // bytes (token 0 code i, token 1 code i) as the low half-word
+        const uint32_t sel = 0x0c0c0000u | static_cast<uint32_t>(4 + i) << 8 | static_cast<uint32_t>(i);
+        const auto t = __builtin_amdgcn_cvt_pk_f32_fp8(
+            __builtin_amdgcn_perm(f.v[1][w], f.v[0][w], sel), false);
+        vp[4 * w + i] = pack_f16x2_int(t[0], t[1]);
+      }
+  }
   if constexpr (KT == kI8) {
 #pragma unroll
     for (int tok = 0; tok < 2; ++tok)
@@ -278,12 +302,12 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
       float part = KT == kI8 ? qb[h] : 0.f;
-      if constexpr (KT == kI8) {
+      if constexpr (KT >= kI8) {
 #pragma unroll
         for (int i = 0; i < 2 * W; ++i) part = dot2_f16(qv[h][i], kp[tok][i], part);
       }
 #pragma unroll
-      for (int w = 0; w < (KT == kI8 ? 0 : W); ++w) {
+      for (int w = 0; w < (KT >= kI8 ? 0 : W); ++w) {
         if constexpr (KT == kBF16) {
           part = dot2_bf16(qv[h][w], f.k[tok][w], part);
         } else {
@@ -311,13 +335,13 @@ __device__ __forceinline__ void softmax_block(const Frag<KT, D>& f,
     }
     const float p0 = exp2_fast(s[0][h] - m[h]);
     const float p1 = exp2_fast(s[1][h] - m[h]);
-    if constexpr (KT == kI8) {
-      // INT8: the weights times the tokens' V scales meet the widened codes
-      // (p * (s * code) = (p * s) * code) as fp16 pairs; the sum takes the
-      // plain weights, rounded the same way.
+    if constexpr (KT >= kI8) {
+      // One-byte codes: the weights times the tokens' V scales meet the
+      // widened codes (p * (s * code) = (p * s) * code) as fp16 pairs; the
+      // sum takes the plain weights, rounded the same way.
       l[h] = dot2_f16(pack_f16x2(p0, p1), kF16OnePair, l[h]);
       const uint32_t pp = pack_f16x2(p0 * f.vs[0], p1 * f.vs[1]);
-      st.vb[h] = dot2_f16(pp, kF16OnePair, st.vb[h]);
+      if constexpr (KT == kI8) st.vb[h] = dot2_f16(pp, kF16OnePair, st.vb[h]);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[h][e] = dot2_f16(pp, vp[e], acc[h][e]);
     } else {
@@ -435,9 +459,9 @@ __device__ __forceinline__ void attend(const PagedLaunch& a, int lane, int b, in
     }
     if constexpr (KT == kI8) unbias(st);
   }
-  if (KT != kI8 && fused) {
+  if (KT < kI8 && fused) {
     // The new rows, as token slot 0 of lane group 0 of a one-token block.
-    // (The INT8 cache has no fused append: its rows must be quantised.)
+    // (One-byte caches have no fused append: their rows must be quantised.)
     using S = RowShape<KT, D>;
     const int blk = wave_uniform(trow[t_last / kBlockTokens]);
     if (blk >= 0 && blk < a.num_blocks) {
@@ -781,7 +805,7 @@ hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
   constexpr bool kWide = KT != kF32 || D < 128;  // register budget allows >= 2 waves
   // INT8 buffers are half the registers of bf16 ones: three fit beside four
   // heads at two waves per SIMD.
-  constexpr int NBUF = (KT == kI8 || (KT == kBF16 && HPW == 1)) ? 3 : 2;
+  constexpr int NBUF = (KT >= kI8 || (KT == kBF16 && HPW == 1)) ? 3 : 2;
   constexpr int WPE = (HPW == 1 && kWide) ? 3 : (kWide ? 2 : 1);
   const int ratio = a.num_q_heads / a.num_kv_heads;
   if (a.counts) {
@@ -827,7 +851,7 @@ bool paged_supported(int head_dim, int ratio, bool /*bf16*/) {
 int max_partition_blocks() { return kMaxPartitionBlocks; }
 
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream) {
-  if (a.int8) return launch_by_dim<kI8>(a, stream);
+  if (a.int8) return a.fp8 ? launch_by_dim<kF8>(a, stream) : launch_by_dim<kI8>(a, stream);
   return a.bf16 ? launch_by_dim<kBF16>(a, stream) : launch_by_dim<kF32>(a, stream);
 }
 

@@ -49,6 +49,7 @@ struct PagedLaunch {
   // per-channel K scales, v_scale [NB, 16, H_kv] the per-token V scales;
   // q and the output are bf16.
   bool int8;
+  bool fp8;  // with int8: the codes are FP8 E4M3, not integers
   const float* k_scale;
   const float* v_scale;
   // Sliding window: each row sees its last `window` positions; 0 = all.
@@ -90,6 +91,7 @@ struct AppendInt8Launch {
   const int32_t* seq_lens;
   int batch, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks;
   bool bf16;
+  bool fp8;  // E4M3 codes (V scale max |v| / 448) instead of INT8 codes
 };
 
 struct CopyBlocksLaunch {

@@ -1,0 +1,179 @@
+"""GPU parity of the FP8 (E4M3) cache path against the fp64 oracle.
+
+The append is compared bit for bit (codes and V scales over the whole
+buffers) with ``oracle.append_paged_fp8``, including exact ties, saturation
+and signed zeros; the decode output elementwise within the contract
+tolerance with ``oracle.decode_attn_paged_fp8`` over the same stored codes.
+Unfilled slots hold the E4M3 NaN code and a NaN scale, so an over-read
+shows up as a NaN output.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from contract import assert_contract
+from gpu_util import down_bits, down_f64, log, up
+from workloads import make_config_inputs, make_paged_decode_fp8
+
+pytestmark = pytest.mark.gpu
+
+kvd = pytest.importorskip("kv_cache_decode_02_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+class Fp8Dev:
+    def __init__(self, inp):
+        self.inp = inp
+        self.q = up(inp.q)
+        self.kq = up(inp.kq_pool)
+        self.vq = up(inp.vq_pool)
+        self.vs = up(inp.vs_pool)
+        self.ks = up(inp.k_scale)
+        self.k_new = up(inp.k_new)
+        self.v_new = up(inp.v_new)
+        self.table = up(inp.block_table)
+        self.seq = up(inp.seq_lens)
+
+    def append(self, k_new=None, v_new=None, ks=None):
+        kvd.kv_append_paged_fp8(self.kq, self.vq, self.vs,
+                                self.k_new if k_new is None else k_new,
+                                self.v_new if v_new is None else v_new,
+                                self.ks if ks is None else ks, self.table, self.seq)
+
+
+def _oracle_step(inp, k_new=None, v_new=None, dtype="bf16", ks=None):
+    return oracle.append_paged_fp8(inp.kq_pool, inp.vq_pool, inp.vs_pool,
+                                   inp.k_new if k_new is None else k_new,
+                                   inp.v_new if v_new is None else v_new, dtype,
+                                   inp.k_scale if ks is None else ks, inp.block_table,
+                                   inp.seq_lens)
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+APPEND_CASES = [
+    ("gqa-d128", dict(B=5, H_q=32, H_kv=8, d=128, lens=[1, 16, 17, 500, 4096])),
+    ("mha-d64", dict(B=3, H_q=4, H_kv=4, d=64, lens=[32, 33, 2])),
+    ("d32", dict(B=2, H_q=2, H_kv=2, d=32, lens=[129, 7])),
+]
+
+
+@pytest.mark.parametrize("name,c", APPEND_CASES, ids=[n for n, _ in APPEND_CASES])
+def test_append_fp8_bit_exact(name, c):
+    log(f"fp8 append {name}")
+    inp = make_paged_decode_fp8(np.random.default_rng(zlib.crc32(name.encode())), c["B"],
+                                c["H_q"], c["H_kv"], c["d"], c["lens"])
+    dev = Fp8Dev(inp)
+    dev.append()
+    torch.cuda.synchronize()
+    kq, vq, vs = _oracle_step(inp)
+    assert np.array_equal(_bits(down_bits(dev.kq)), _bits(kq))
+    assert np.array_equal(_bits(down_bits(dev.vq)), _bits(vq))
+    assert np.array_equal(_bits(down_bits(dev.vs)), _bits(vs))
+
+
+def test_append_fp8_ties_saturation_and_signed_zero():
+    # fp32 rows whose K quotients (power-of-two scales: exact) sit on E4M3
+    # midpoints, beyond 448, or round to -0; one all-zero V row.
+    log("fp8 append f32 ties")
+    rng = np.random.default_rng(4)
+    B, H_kv, d = 2, 2, 32
+    inp = make_paged_decode_fp8(rng, B, 4, H_kv, d, [20, 3])
+    ks = np.full((H_kv, d), 0.25, np.float32)
+    vals = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    pick = np.concatenate([mids, [460.0, 1000.0, 2.0 ** -11, 448.0]]).astype(np.float32)
+    y = rng.choice(pick, size=(B, H_kv, d)) * rng.choice([-1.0, 1.0], size=(B, H_kv, d))
+    k_new = (y.astype(np.float32) * ks).astype(np.float32)
+    v_new = rng.standard_normal((B, H_kv, d)).astype(np.float32)
+    v_new[1, 0] = 0.0
+    dev = Fp8Dev(inp)
+    dev.append(up(k_new), up(v_new), up(ks))
+    torch.cuda.synchronize()
+    kq, vq, vs = _oracle_step(inp, k_new, v_new, "f32", ks)
+    assert np.array_equal(_bits(down_bits(dev.kq)), _bits(kq))
+    assert np.array_equal(_bits(down_bits(dev.vq)), _bits(vq))
+    assert np.array_equal(_bits(down_bits(dev.vs)), _bits(vs))
+
+
+DECODE_CASES = [
+    ("gqa-r4-ragged", dict(B=6, H_q=32, H_kv=8, d=128, lens=[1, 15, 17, 511, 3000, 4096], pt=0)),
+    ("gqa-r4-pt256", dict(B=4, H_q=32, H_kv=8, d=128, lens=[16, 513, 2049, 100], pt=256)),
+    ("mha-d128", dict(B=2, H_q=8, H_kv=8, d=128, lens=[1000, 77], pt=0)),
+    ("r2-d64", dict(B=3, H_q=8, H_kv=4, d=64, lens=[33, 999, 1], pt=0)),
+    ("r8-d128", dict(B=2, H_q=64, H_kv=8, d=128, lens=[2500, 300], pt=0)),
+    ("mqa-d32", dict(B=2, H_q=4, H_kv=1, d=32, lens=[129, 640], pt=64)),
+]
+
+
+@pytest.mark.parametrize("name,c", DECODE_CASES, ids=[n for n, _ in DECODE_CASES])
+def test_decode_fp8_parity(name, c):
+    log(f"fp8 decode {name}")
+    inp = make_paged_decode_fp8(np.random.default_rng(zlib.crc32(name.encode()) + 11), c["B"],
+                                c["H_q"], c["H_kv"], c["d"], c["lens"])
+    dev = Fp8Dev(inp)
+    dev.append()
+    out = kvd.decode_attn_paged_fp8(dev.q, dev.kq, dev.vq, dev.ks, dev.vs, dev.table, dev.seq,
+                                    inp.max_seq_len, partition_tokens=c["pt"])
+    torch.cuda.synchronize()
+    kq, vq, vs = _oracle_step(inp)
+    ref = oracle.decode_attn_paged_fp8(inp.q, kq, vq, vs, inp.k_scale, inp.block_table,
+                                       inp.seq_lens, "bf16")
+    rep = assert_contract(down_f64(out), ref, name)
+    log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")
+
+
+def test_fp8_phases_equal_single_call():
+    log("fp8 partials + merge")
+    inp = make_paged_decode_fp8(np.random.default_rng(22), 4, 32, 8, 128, [900, 40, 2049, 16])
+    dev = Fp8Dev(inp)
+    dev.append()
+    one = kvd.decode_attn_paged_fp8(dev.q, dev.kq, dev.vq, dev.ks, dev.vs, dev.table, dev.seq,
+                                    inp.max_seq_len)
+    ws = kvd.alloc_workspace(inp.B, 32, 8, 128, inp.max_seq_len)
+    kvd.decode_attn_paged_fp8_partials(dev.q, dev.kq, dev.vq, dev.ks, dev.vs, dev.table,
+                                       dev.seq, inp.max_seq_len, ws)
+    two = torch.empty_like(dev.q)
+    kvd.decode_attn_merge(two, dev.seq, 8, inp.max_seq_len, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+
+
+def test_fp8_full_size_sampled():
+    name = "gqa_llama3_8b_fp8"
+    log(f"full {name}: generating")
+    inp = make_config_inputs(name)[0]
+    dev = Fp8Dev(inp)
+    dev.append()
+    out = kvd.decode_attn_paged_fp8(dev.q, dev.kq, dev.vq, dev.ks, dev.vs, dev.table, dev.seq,
+                                    inp.max_seq_len)
+    torch.cuda.synchronize()
+    got = down_f64(out)
+    assert np.all(np.isfinite(got))
+    kq, vq, vs = _oracle_step(inp)
+    r = inp.H_q // inp.H_kv
+    rng = np.random.default_rng(2)
+    picks = [(0, 0), (inp.B - 1, inp.H_kv - 1)] + [
+        (int(rng.integers(inp.B)), int(rng.integers(inp.H_kv))) for _ in range(4)]
+    for b, g in picks:
+        n = int(inp.seq_lens[b])
+        K = (oracle.e4m3_decode(oracle.gather_logical(kq[:, :, g:g + 1], inp.block_table, b, n))
+             * inp.k_scale[g:g + 1].astype(np.float64))
+        V = (oracle.e4m3_decode(oracle.gather_logical(vq[:, :, g:g + 1], inp.block_table, b, n))
+             * oracle.gather_logical(vs[:, :, g:g + 1], inp.block_table, b, n)
+             .astype(np.float64)[..., None])
+        q = oracle.to_f64(inp.q[b, g * r:(g + 1) * r], "bf16")
+        assert_contract(got[b, g * r:(g + 1) * r], oracle.decode_attention(q, K, V),
+                        f"{name} b={b} g={g}")
+    log(f"full {name}: ok")

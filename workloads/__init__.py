@@ -14,6 +14,7 @@ from .gen import (
     make_paged_decode,
     PagedInt8Inputs,
     make_paged_decode_int8,
+    make_paged_decode_fp8,
     PagedPrefillInputs,
     make_paged_prefill,
     make_mla,
@@ -24,7 +25,8 @@ from .configs import CONFIGS, config, make_config_inputs
 
 __all__ = [
     "PagedDecodeInputs", "MlaInputs", "bf16_round_bits", "make_paged_decode",
-    "PagedInt8Inputs", "make_paged_decode_int8", "PagedPrefillInputs", "make_paged_prefill",
+    "PagedInt8Inputs", "make_paged_decode_int8", "make_paged_decode_fp8", "PagedPrefillInputs",
+    "make_paged_prefill",
     "make_mla", "BLOCK_SIZE", "UNUSED_TABLE_ENTRY", "CONFIGS", "config",
     "make_config_inputs",
 ]

@@ -17,20 +17,24 @@
                   the gqa_llama3_8b batch (same seed, so the same lengths)
                   over an INT8 cache: per-channel K and per-token V scales,
                   bf16 queries and output
+  gqa_llama3_8b_fp8
+                  the same batch over an FP8 (E4M3) cache with the same
+                  scale layout
   prefill_llama3_8b
                   chunked prefill on the Llama-3-8B shape (H_q = 32, H_kv =
                   8, d_head = 128): 4 sequences with 0 / 2048 / 4096 / 6144
                   cached positions each take a 2048-token chunk, bf16 N(0,1)
 
 Seeds: config k (1..5 in the order above, 6 for the prefill) uses numpy
-default_rng(42 + k), the INT8 batch the GQA batch's seed; 42
+default_rng(42 + k), the INT8 and FP8 batches the GQA batch's seed; 42
 is the seed of the pages' own numpy sketch.  Lengths are drawn first, then the
 generator's fixed draw order (``workloads.gen``).
 """
 
 import numpy as np
 
-from .gen import make_paged_decode, make_paged_decode_int8, make_paged_prefill, make_mla
+from .gen import (make_mla, make_paged_decode, make_paged_decode_fp8, make_paged_decode_int8,
+                  make_paged_prefill)
 
 CONFIGS = {
     "tiny": dict(index=1, kind="paged", B=1, H_q=4, H_kv=4, d=32, layers=2,
@@ -51,6 +55,9 @@ CONFIGS = {
     "gqa_llama3_8b_int8": dict(index=3, kind="paged_int8", B=64, H_q=32, H_kv=8, d=128,
                                layers=1, lens=("uniform", 512, 8192), dtype="int8",
                                table="permuted", std=1.0, partition=0),
+    "gqa_llama3_8b_fp8": dict(index=3, kind="paged_fp8", B=64, H_q=32, H_kv=8, d=128,
+                              layers=1, lens=("uniform", 512, 8192), dtype="fp8",
+                              table="permuted", std=1.0, partition=0),
     "prefill_llama3_8b": dict(index=6, kind="prefill", B=4, H_q=32, H_kv=8, d=128, layers=1,
                               lens=("list", (0, 2048, 4096, 6144)), new=2048, dtype="bf16",
                               table="permuted", std=1.0, partition=0),
@@ -97,10 +104,10 @@ def make_config_inputs(name, sentinel="nan", rng=None):
                                              [cfg["new"]] * B, dtype=cfg["dtype"],
                                              table=cfg["table"], std=cfg["std"],
                                              sentinel=sentinel))
-        elif cfg["kind"] == "paged_int8":
-            layers.append(make_paged_decode_int8(rng, B, cfg["H_q"], cfg["H_kv"], cfg["d"], lens,
-                                                 table=cfg["table"], std=cfg["std"],
-                                                 sentinel=sentinel))
+        elif cfg["kind"] in ("paged_int8", "paged_fp8"):
+            gen = make_paged_decode_int8 if cfg["kind"] == "paged_int8" else make_paged_decode_fp8
+            layers.append(gen(rng, B, cfg["H_q"], cfg["H_kv"], cfg["d"], lens, table=cfg["table"],
+                              std=cfg["std"], sentinel=sentinel))
         else:
             layers.append(make_mla(rng, B, cfg["H"], cfg["d_c"], cfg["d_rope"], lens,
                                    std=cfg["std"], table=cfg["table"], sentinel=sentinel))

@@ -33,6 +33,14 @@ bf16 draws (the append quantises them).  Unfilled slots hold code -128 (never
 written by the append) and a NaN V scale in parity runs, code 0 and scale 0
 in timing runs.  Draw order: block permutation, q, K codes, V codes, V
 scales, K scales, k_new, v_new.
+
+FP8 caches (``make_paged_decode_fp8``) hold E4M3 bytes: a uniform sign and a
+magnitude code uniform in 0x00 .. 0x3F (the values 0 .. 1.875, from 2^-9 up
+through the subnormals and eight binades), K and V scales uniform in
+std * [0.5, 1.5], so that the cached values again have roughly the spread of
+the bf16 workloads.  Unfilled slots hold code 0x7F (E4M3 NaN, never written
+by the append) and a NaN V scale in parity runs, code 0 and scale 0 in timing
+runs.  Same draw order as the INT8 caches.
 """
 
 from dataclasses import dataclass
@@ -261,6 +269,7 @@ class PagedInt8Inputs:
     k_new: np.ndarray    # bf16 bits [B, H_kv, d]
     v_new: np.ndarray    # bf16 bits [B, H_kv, d]
     dtype: str = "bf16"  # of q, k_new, v_new and the output
+    codes: str = "int8"  # "int8" codes, or "fp8": uint8 E4M3 bytes
 
     @property
     def max_blocks_per_seq(self):
@@ -305,6 +314,47 @@ def make_paged_decode_int8(rng, B, H_q, H_kv, d, seq_lens, table="permuted", std
     _mark_unfilled(vs, owned, lens, block_size, scale)
     return PagedInt8Inputs(B, H_q, H_kv, d, block_size, lens.astype(np.int32), bt, nb, q, kq, vq,
                            vs, ks, k_new, v_new)
+
+
+def _fp8_codes(rng, shape):
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for start in range(0, n, _CHUNK):
+        stop = min(start + _CHUNK, n)
+        out[start:stop] = rng.integers(0, 0x80, size=stop - start, dtype=np.uint8)
+    # bit 7: sign; bits 0-5: magnitude code 0x00 .. 0x3F (bit 6 cleared)
+    return (out & np.uint8(0xBF)).reshape(shape)
+
+
+def make_paged_decode_fp8(rng, B, H_q, H_kv, d, seq_lens, table="permuted", std=1.0,
+                          sentinel="nan", max_blocks_per_seq=None, block_size=BLOCK_SIZE):
+    """Draw one decode step's inputs over an FP8 (E4M3) cache (see the module
+    docstring)."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if lens.shape != (B,) or np.any(lens < 1):
+        raise ValueError("seq_lens must have B entries, each >= 1")
+    if H_q % H_kv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    mb = max_blocks_per_seq or _blocks_needed(lens.max(), block_size)
+    bt, nb, owned = _assign_blocks(rng, lens, block_size, mb, table)
+    q = _draw(rng, (B, H_q, d), std, "bf16")
+    kq = _fp8_codes(rng, (nb, block_size, H_kv, d))
+    vq = _fp8_codes(rng, (nb, block_size, H_kv, d))
+    vs = _scales(rng, (nb, block_size, H_kv), std * 64.0)
+    ks = _scales(rng, (H_kv, d), std * 64.0)
+    k_new = _draw(rng, (B, H_kv, d), std, "bf16")
+    v_new = _draw(rng, (B, H_kv, d), std, "bf16")
+    if sentinel == "nan":
+        code, scale = np.uint8(0x7F), np.float32(np.nan)
+    elif sentinel == "zero":
+        code, scale = np.uint8(0), np.float32(0)
+    else:
+        raise ValueError(f"unknown sentinel {sentinel!r}")
+    _mark_unfilled(kq, owned, lens, block_size, code)
+    _mark_unfilled(vq, owned, lens, block_size, code)
+    _mark_unfilled(vs, owned, lens, block_size, scale)
+    return PagedInt8Inputs(B, H_q, H_kv, d, block_size, lens.astype(np.int32), bt, nb, q, kq, vq,
+                           vs, ks, k_new, v_new, codes="fp8")
 
 
 @dataclass

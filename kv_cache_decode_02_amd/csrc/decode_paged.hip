@@ -62,8 +62,8 @@ struct RowShape {
   static constexpr int CW = W < 4 ? W : 4;  // words per vector load
   static constexpr int NCH = W / CW;        // vector loads per row per lane
   static constexpr int RW = D / EPW;        // words per row (one head)
-  // Query words per lane: INT8 codes are widened to bf16 pairs, so each code
-  // word meets two words of (scaled) query.
+  // Query words per lane: one-byte codes are widened to fp16 pairs, so each
+  // code word meets two words of (scaled) query.
   static constexpr int QW = KT >= kI8 ? 2 * W : W;
   static_assert(W >= 1 && W % CW == 0, "unsupported head_dim");
   // Word offset, inside a row, of the lane's chunk c.
@@ -130,8 +130,8 @@ __device__ __forceinline__ void unbias(HeadState<HPW, DPL>& st) {
   }
 }
 
-// The K and V rows of the lane's two token slots of one block (INT8: codes,
-// and the two tokens' V scales).
+// The K and V rows of the lane's two token slots of one block (one-byte
+// caches: codes, and the two tokens' V scales).
 template <int KT, int D>
 struct Frag {
   uint32_t k[2][RowShape<KT, D>::W];
@@ -140,7 +140,7 @@ struct Frag {
 };
 
 // Query slice of heads h0 .. h0 + HPW - 1 of sequence b, in the lane layout of
-// the K rows.  INT8 cache: the query is bf16 and is multiplied by KV head g's
+// the K rows.  One-byte caches: the query is bf16 and is multiplied by KV head g's
 // per-channel K scales (q . (s * code) = (q * s) . code), then rounded to
 // fp16 pairs that meet the widened codes in dot2 (fp16 keeps 11 bits of the
 // scaled query; bf16's 8 would cost ~0.5% in the scores).
@@ -803,8 +803,8 @@ hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
 template <int KT, int D, int HPW>
 hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
   constexpr bool kWide = KT != kF32 || D < 128;  // register budget allows >= 2 waves
-  // INT8 buffers are half the registers of bf16 ones: three fit beside four
-  // heads at two waves per SIMD.
+  // One-byte buffers are half the registers of bf16 ones: three fit beside
+  // four heads at two waves per SIMD.
   constexpr int NBUF = (KT >= kI8 || (KT == kBF16 && HPW == 1)) ? 3 : 2;
   constexpr int WPE = (HPW == 1 && kWide) ? 3 : (kWide ? 2 : 1);
   const int ratio = a.num_q_heads / a.num_kv_heads;

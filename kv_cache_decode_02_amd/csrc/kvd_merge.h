@@ -20,6 +20,34 @@ struct MergeShape {
   static constexpr int kRows = 8;                         // rows in flight
 };
 
+// The lane's DL consecutive floats of a piece row, as 16-byte (or 8-byte)
+// vector loads, or zeros when `take` is false.
+template <int DL>
+__device__ __forceinline__ void load_row(float (&dst)[DL], const float* src, bool take) {
+  if (take) {
+    if constexpr (DL % 4 == 0) {
+#pragma unroll
+      for (int d = 0; d < DL; d += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + d);
+        dst[d] = v.x;
+        dst[d + 1] = v.y;
+        dst[d + 2] = v.z;
+        dst[d + 3] = v.w;
+      }
+    } else if constexpr (DL == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(src);
+      dst[0] = v.x;
+      dst[1] = v.y;
+    } else {
+#pragma unroll
+      for (int d = 0; d < DL; ++d) dst[d] = src[d];
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < DL; ++d) dst[d] = 0.f;
+  }
+}
+
 // One wave combines pieces [0, np) of one (b, h): `ml` holds their (m, l)
 // pairs and `o` their rows of D floats.  On return lane `lane` holds dims
 // lane * DL .. of the unnormalised sum and every lane the denominator.
@@ -35,10 +63,7 @@ __device__ __forceinline__ void merge_pieces(const float2* ml, const float* o, i
     const float2 v = lane < np ? ml[lane] : make_float2(kMinusBig, 0.f);
     float rows[kRows][DL];
 #pragma unroll
-    for (int k = 0; k < kRows; ++k)
-#pragma unroll
-      for (int d = 0; d < DL; ++d)
-        rows[k][d] = (k < np && active) ? o[k * D + lane * DL + d] : 0.f;
+    for (int k = 0; k < kRows; ++k) load_row<DL>(rows[k], o + k * D + lane * DL, k < np && active);
     float M = v.y > 0.f ? v.x : kMinusBig;
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
@@ -80,9 +105,7 @@ __device__ __forceinline__ void merge_pieces(const float2* ml, const float* o, i
       float rows[kRows][DL];
 #pragma unroll
       for (int k = 0; k < kRows; ++k)
-#pragma unroll
-        for (int d = 0; d < DL; ++d)
-          rows[k][d] = (idx[k] >= 0 && active) ? o[(p0 + idx[k]) * D + lane * DL + d] : 0.f;
+        load_row<DL>(rows[k], o + (p0 + max(idx[k], 0)) * D + lane * DL, idx[k] >= 0 && active);
 #pragma unroll
       for (int k = 0; k < kRows; ++k) {
         const float w = __shfl(w_lane, idx[k] >= 0 ? idx[k] : 0, kWave);

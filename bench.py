@@ -117,38 +117,45 @@ def queue_ahead(torch, stream, ms):
     return lambda: a.elapsed_time(b) / 1e3  # seconds the spin held the device
 
 
-def time_graph(torch, step, out, args):
-    """Capture one step (append, partials, merge) in a HIP graph, check that
+def time_graph(torch, step, out, args, variants=1):
+    """Capture the step (append, partials, merge) in HIP graphs, check that
     replays give the eager step's output bit for bit (with eager work between
-    replays), then time args.steps replays.  Returns (ms per step, True)."""
+    replays), then time args.steps replays.  ``step(i)`` takes the step's index;
+    with ``variants`` > 1 the steps differ with i % variants (e.g. rotating
+    cache copies), so one graph is captured per variant and step i replays
+    graph i % variants.  Returns (ms per step, True)."""
     stream = torch.cuda.current_stream()
-    step()
-    torch.cuda.synchronize()
-    ref = out.clone()
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step()  # first run on the capture stream outside the capture
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        step()
+    graphs, refs = [], []
+    for v in range(variants):
+        step(v)
+        torch.cuda.synchronize()
+        refs.append(out.clone())
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(v)  # first run on the capture stream outside the capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step(v)
+        graphs.append(g)
     for _ in range(3):
-        out.zero_()
-        g.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(out, ref):
-            raise RuntimeError("graph replay differs from the eager step")
-        step()  # eager work between replays
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        g.replay()
+        for v, g in enumerate(graphs):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, refs[v]):
+                raise RuntimeError("graph replay differs from the eager step")
+            step(v)  # eager work between replays
+            torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % variants].replay()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
-        g.replay()
+    for i in range(args.steps):
+        graphs[i % variants].replay()
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / args.steps, True
@@ -324,7 +331,7 @@ def main_int8(args, kvd, make_config_inputs):
     part_avg = float(np.mean(part_ms))
     ms_step, graph_check = ms_eager, None
     if not args.no_graph:
-        ms_step, graph_check = time_graph(torch, step, out, args)
+        ms_step, graph_check = time_graph(torch, lambda i: step(), out, args)
     kv_bytes = inp.kv_bytes_read
     kernel = "paged_balanced" if pt_used == 0 else "paged_partials"
     value = kv_bytes / (ms_step / 1e3) / 1e9
@@ -454,7 +461,7 @@ def main_prefill(args, kvd, make_config_inputs):
     part_avg = float(np.mean(part_ms))
     ms_step, graph_check = ms_eager, None
     if not args.no_graph:
-        ms_step, graph_check = time_graph(torch, step, out, args)
+        ms_step, graph_check = time_graph(torch, lambda i: step(), out, args)
     flops = prefill_flops(inp)
     value = flops / (ms_step / 1e3) / 1e12
     achieved = flops / (part_avg / 1e3) / 1e12
@@ -528,8 +535,12 @@ def main_mla(args, kvd, make_config_inputs):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0 - spin_s()
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_eager = start.elapsed_time(end) / args.steps
     part_avg = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_step, graph_check = ms_eager, None
+    if not args.no_graph:
+        # one graph per cache copy; step i replays the graph of copy i % copies
+        ms_step, graph_check = time_graph(torch, step, out, args, variants=len(caches))
     kv_bytes = inp.kv_bytes_read
     positions = int(inp.seq_lens.astype(np.int64).sum())
     flops = positions * H * (inp.width + inp.d_c) * 2
@@ -540,6 +551,9 @@ def main_mla(args, kvd, make_config_inputs):
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "step_launch": "hip graph" if not args.no_graph else "eager",
+        "step_kernels": "kv_append_paged, decode_attn_mla_partials, merge",
+        "ms_per_step_eager": round(ms_eager, 5), "graph_replays_match_eager": graph_check,
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": H, "d_c": inp.d_c,
                    "d_rope": inp.d_rope, "block_size": 16, "sum_seq_len": positions,
@@ -640,7 +654,7 @@ def main():
     part_avg = float(np.mean(part_ms))
     ms_step, graph_check = ms_eager, None
     if not args.no_graph:
-        ms_step, graph_check = time_graph(torch, step, out, args)
+        ms_step, graph_check = time_graph(torch, lambda i: step(), out, args)
 
     kv_bytes = inp.kv_bytes_read
     step_s = ms_step / 1e3

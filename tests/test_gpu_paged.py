@@ -98,6 +98,12 @@ DECODE_CASES = [
     ("f32-d128", dict(B=2, H_q=4, H_kv=2, d=128, lens=[77, 640], pt=0, dtype="f32")),
     ("f32-d64-r8", dict(B=2, H_q=16, H_kv=2, d=64, lens=[5, 1500], pt=0, dtype="f32")),
     ("f32-d32-r1", dict(B=3, H_q=4, H_kv=4, d=32, lens=[1, 129, 130], pt=0, dtype="f32")),
+    # the largest group (64 query heads on one K/V head: 16 wavefronts of 4 heads)
+    ("r64-mqa", dict(B=2, H_q=64, H_kv=1, d=128, lens=[700, 33], pt=0)),
+    # groups of 12: three 4-head wavefronts per K/V head, two idle wavefronts per
+    # 8-wave workgroup
+    ("r12-balanced", dict(B=3, H_q=24, H_kv=2, d=64, lens=[257, 40, 1600], pt=0)),
+    ("r12-split256", dict(B=3, H_q=24, H_kv=2, d=64, lens=[257, 40, 1600], pt=256)),
 ]
 
 
@@ -280,6 +286,25 @@ def test_empty_batch_is_a_no_op():
     seq = torch.zeros((0,), dtype=torch.int32, device="cuda")
     out = kvd.decode_attn_paged(q, kc, kc.clone(), table, seq, 16)
     assert out.shape == (0, 8, 128)
+
+
+@pytest.mark.parametrize("B", [8191, 8193])
+def test_batch_around_the_balanced_split_limit(B):
+    # The automatic mode splits batches of up to 8191 sequences evenly (their
+    # prefix sums fill 64 KiB of LDS) and larger ones in fixed partitions.
+    # Both sides of the limit, checked on a sample of sequences (each
+    # sequence's output depends on its own rows only).
+    log(f"batch {B}")
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 49, size=B)
+    inp = make_paged_decode(rng, B, 8, 2, 64, lens)
+    dev = Paged(inp)
+    got = down_f64(_run_step(dev, 0))
+    sel = np.unique(np.concatenate([[0, B - 1], rng.integers(0, B, size=62)]))
+    ref = oracle.decode_attn_paged(inp.q[sel], inp.k_pool, inp.v_pool, inp.block_table[sel],
+                                   inp.seq_lens[sel], inp.dtype, inp.k_new[sel], inp.v_new[sel])
+    rep = assert_contract(got[sel], ref, f"batch {B}")
+    log(f"  {len(sel)} sequences, max_err {rep['max_err']:.3e}")
 
 
 # --- full-size workloads, sampled -----------------------------------------------

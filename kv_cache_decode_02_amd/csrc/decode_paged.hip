@@ -798,8 +798,12 @@ hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
 
 // Tuned on MI355X (bf16, d_head 128): one head per wave keeps 3 waves per
 // SIMD; four heads per wave need ~200 VGPRs (2 waves per SIMD) and do best
-// with two buffers.  Eight-wave workgroups help when a group's rows are read
-// by several wavefronts (one head per wave, or head chunks of one group).
+// with two buffers.  With one head per wave, eight-wave workgroups read whole
+// token rows of every block together.  Head chunks of one group share a
+// workgroup of four waves when they fit in it: its finer grain (half the
+// blocks of an eight-wave one) shortens the tail of long fixed partitions;
+// larger groups take eight waves, so that a block's second and later reads
+// stay in one XCD's L2.
 template <int KT, int D, int HPW>
 hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
   constexpr bool kWide = KT != kF32 || D < 128;  // register budget allows >= 2 waves
@@ -814,7 +818,7 @@ hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
     return launch_balanced<KT, D, HPW, NBUF, WPE, 4>(a, stream);
   }
   if constexpr (kWide) {
-    if (HPW == 1 || ratio > HPW) return launch_variant<KT, D, HPW, NBUF, WPE, 8>(a, stream);
+    if (HPW == 1 || ratio > 4 * HPW) return launch_variant<KT, D, HPW, NBUF, WPE, 8>(a, stream);
   }
   return launch_variant<KT, D, HPW, NBUF, WPE, 4>(a, stream);
 }

@@ -512,11 +512,19 @@ def main_mla(args, kvd, make_config_inputs):
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        # The default step is the partials kernel with the append fused in (it
+        # takes the new rows from c_new and writes them into their slots),
+        # then the merge; --separate-append runs kv_append_paged first.
         c = caches[i % len(caches)]
-        kvd.kv_append_paged(c[:, :, None, :], None, c_new, None, table, seq)
+        if args.separate_append:
+            kvd.kv_append_paged(c[:, :, None, :], None, c_new, None, table, seq)
         if ev is not None:
             ev[0].record(stream)
-        kvd.decode_attn_mla_partials(q, c, table, seq, L, ws, partition_tokens=pt)
+        if args.separate_append:
+            kvd.decode_attn_mla_partials(q, c, table, seq, L, ws, partition_tokens=pt)
+        else:
+            kvd.decode_attn_mla_append_partials(q, c, c_new[:, 0], table, seq, L, ws,
+                                                partition_tokens=pt)
         if ev is not None:
             ev[1].record(stream)
         kvd.decode_attn_merge(out, seq, 1, L, ws, partition_tokens=pt)
@@ -552,7 +560,8 @@ def main_mla(args, kvd, make_config_inputs):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "step_launch": "hip graph" if not args.no_graph else "eager",
-        "step_kernels": "kv_append_paged, decode_attn_mla_partials, merge",
+        "step_kernels": ("kv_append_paged, decode_attn_mla_partials, merge" if args.separate_append
+                         else "decode_attn_mla_append_partials (append fused), merge"),
         "ms_per_step_eager": round(ms_eager, 5), "graph_replays_match_eager": graph_check,
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.B, "num_q_heads": H, "d_c": inp.d_c,

@@ -334,6 +334,42 @@ int decode_attn_mla_partials(const void* q, const void* c_cache,
                              size_t workspace_bytes, void* stream);
 
 /*
+ * decode_attn_mla_append -- kv_append_paged of this step's latent rows
+ * followed by decode_attn_mla, in one pass: the MLA cache of "KV Cache（键值
+ * 缓存）" (2.2 路线一: one latent row per token and layer) grown by the
+ * decode step's in-place slot write ("单请求 KV Cache", 生产系统的做法).
+ * Position seq_lens[b] - 1 takes its row from c_new (read once, used in the
+ * scores and the values like any cached row) and the row is written into its
+ * cache slot as kv_append_paged would write it; the other positions are read
+ * from the cache.  The result equals the two separate calls up to the order
+ * of floating-point accumulation.
+ *   c_new    [batch, d_c + d_rope] bf16, 16-byte aligned
+ *   c_cache  is written (the new rows' slots only)
+ * Other arguments, sizes, workspace and errors as for decode_attn_mla.  Rows
+ * are written and used only for sequences with 1 <= seq_lens[b] <=
+ * min(max_seq_len, 16 * max_blocks_per_seq) whose last block is inside the
+ * pool; the block holding the new position must not be shared.
+ */
+int decode_attn_mla_append(void* out, const void* q, void* c_cache, const void* c_new,
+                           const int32_t* block_table, const int32_t* seq_lens, int batch,
+                           int num_q_heads, int d_c, int d_rope, int block_size,
+                           int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                           int partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * decode_attn_mla_append_partials -- first phase of decode_attn_mla_append
+ * only (same arguments minus `out`); finish with decode_attn_merge as after
+ * decode_attn_mla_partials.
+ */
+int decode_attn_mla_append_partials(const void* q, void* c_cache, const void* c_new,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int batch, int num_q_heads, int d_c, int d_rope,
+                                    int block_size, int max_blocks_per_seq, int num_blocks,
+                                    int max_seq_len, float scale, int partition_tokens,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * INT8 KV cache ("KV-Cache——为什么AI回复越来越快", KV-Cache量化: one byte per
  * element halves the cache and the bytes a decode step reads; K is scaled per
  * channel, every dimension of a K/V head having its own scale, and V per

@@ -26,6 +26,8 @@ from ._native import (
     alloc_workspace,
     decode_attn_mla,
     decode_attn_mla_partials,
+    decode_attn_mla_append,
+    decode_attn_mla_append_partials,
     mla_default_scale,
     kv_append_paged_int8,
     decode_attn_paged_int8,
@@ -50,7 +52,8 @@ __all__ = [
     "decode_attn_paged_append", "decode_attn_paged_append_partials",
     "decode_attn_paged_window", "decode_attn_paged_window_partials",
     "decode_attn_merge", "decode_attn_workspace_bytes", "decode_attn_partition_tokens",
-    "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials", "mla_default_scale",
+    "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials",
+    "decode_attn_mla_append", "decode_attn_mla_append_partials", "mla_default_scale",
     "kv_append_paged_int8", "decode_attn_paged_int8", "decode_attn_paged_int8_partials",
     "kv_append_paged_fp8", "decode_attn_paged_fp8", "decode_attn_paged_fp8_partials",
     "kv_copy_blocks", "kv_append_paged_multi", "prefill_attn_paged", "block_hashes",

@@ -56,6 +56,12 @@ lib.decode_attn_mla.restype = _i
 lib.decode_attn_mla.argtypes = [_vp] + _MLA_ARGS
 lib.decode_attn_mla_partials.restype = _i
 lib.decode_attn_mla_partials.argtypes = _MLA_ARGS
+# q, c_cache, c_new, then the MLA arguments from block_table on
+_MLA_APPEND_ARGS = _MLA_ARGS[:2] + [_vp] + _MLA_ARGS[2:]
+lib.decode_attn_mla_append.restype = _i
+lib.decode_attn_mla_append.argtypes = [_vp] + _MLA_APPEND_ARGS
+lib.decode_attn_mla_append_partials.restype = _i
+lib.decode_attn_mla_append_partials.argtypes = _MLA_APPEND_ARGS
 lib.kv_append_paged_int8.restype = _i
 lib.kv_append_paged_int8.argtypes = [_vp] * 8 + [_i] * 7 + [_vp]
 # q, k_cache, v_cache, k_scale, v_scale, then the paged arguments from block_table on
@@ -382,6 +388,43 @@ def decode_attn_mla_partials(q, c_cache, block_table, seq_lens, max_seq_len, wor
     args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
                      partition_tokens, workspace)
     _check(lib.decode_attn_mla_partials(*args, _stream(stream)), "decode_attn_mla_partials")
+
+
+def _mla_append_args(q, c_cache, c_new, block_table, seq_lens, max_seq_len, d_c, scale,
+                     partition_tokens, ws):
+    args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
+                     partition_tokens, ws)
+    _need(c_new, "c_new", dtype=torch.bfloat16)
+    if c_new.numel() != q.shape[0] * q.shape[2]:
+        raise KvdError("c_new must be [B, d_c + d_rope] (one latent row per sequence)")
+    return args[:2] + [_ptr(c_new)] + args[2:]
+
+
+def decode_attn_mla_append(q, c_cache, c_new, block_table, seq_lens, max_seq_len, d_c=MLA_D_C,
+                           scale=None, partition_tokens=0, workspace=None, out=None,
+                           stream=None):
+    """kv_append_paged of c_new [B, d_c + d_rope] + decode_attn_mla in one pass:
+    writes each row into its slot and attends over the history plus it."""
+    B, h, _ = q.shape
+    if workspace is None:
+        workspace = alloc_workspace(B, h, 1, d_c, max_seq_len, partition_tokens, device=q.device)
+    if out is None:
+        out = torch.empty((B, h, d_c), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", dtype=torch.bfloat16)
+    args = _mla_append_args(q, c_cache, c_new, block_table, seq_lens, max_seq_len, d_c, scale,
+                            partition_tokens, workspace)
+    _check(lib.decode_attn_mla_append(_ptr(out), *args, _stream(stream)), "decode_attn_mla_append")
+    return out
+
+
+def decode_attn_mla_append_partials(q, c_cache, c_new, block_table, seq_lens, max_seq_len,
+                                    workspace, d_c=MLA_D_C, scale=None, partition_tokens=0,
+                                    stream=None):
+    """First phase of decode_attn_mla_append only (the append included)."""
+    args = _mla_append_args(q, c_cache, c_new, block_table, seq_lens, max_seq_len, d_c, scale,
+                            partition_tokens, workspace)
+    _check(lib.decode_attn_mla_append_partials(*args, _stream(stream)),
+           "decode_attn_mla_append_partials")
 
 
 # --- INT8 cache -----------------------------------------------------------------

@@ -796,6 +796,7 @@ static int mla_setup(const void* q, const void* c_cache, const int32_t* block_ta
   a->partition_tokens = s->pt;
   a->num_partitions = s->parts;
   a->scale = scale;
+  a->c_new = nullptr;
   return KVD_OK;
 }
 
@@ -843,5 +844,59 @@ int decode_attn_mla(void* out, const void* q, const void* c_cache,
                                      workspace, KVD_BF16, s);
   return hip_status(launch_merge(m, st));
 }
+
+// MLA with the append fused in: the checks of decode_attn_mla plus the new
+// rows; launches the partials (and the merge when `out` is given).
+static int mla_append_impl(void* out, const void* q, void* c_cache, const void* c_new,
+                           const int32_t* block_table, const int32_t* seq_lens, int batch,
+                           int num_q_heads, int d_c, int d_rope, int block_size,
+                           int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                           int partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream, bool merge) {
+  Sizes s;
+  MlaLaunch a;
+  int rc = mla_setup(q, c_cache, block_table, seq_lens, batch, num_q_heads, d_c, d_rope,
+                     block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale,
+                     partition_tokens, workspace, workspace_bytes, &s, &a);
+  if (rc || batch == 0) return rc;
+  if (!c_new || (merge && !out)) return KVD_ERR_NULL;
+  if (!aligned16(c_new)) return KVD_ERR_SHAPE;
+  rc = preconditions(seq_lens, block_table, nullptr, batch, max_blocks_per_seq, num_blocks,
+                     max_seq_len, true,
+                     {{q, bytes_of(batch, num_q_heads, d_c + d_rope, KVD_BF16), KVD_BF16},
+                      {c_new, bytes_of(batch, 1, d_c + d_rope, KVD_BF16), KVD_BF16}},
+                     stream);
+  if (rc) return rc;
+  a.c_new = c_new;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(launch_mla_partials(a, st));
+  if (rc || !merge) return rc;
+  const MergeLaunch m = merge_launch(out, seq_lens, batch, num_q_heads, d_c, max_seq_len,
+                                     workspace, KVD_BF16, s);
+  return hip_status(launch_merge(m, st));
+}
+
+int decode_attn_mla_append_partials(const void* q, void* c_cache, const void* c_new,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int batch, int num_q_heads, int d_c, int d_rope,
+                                    int block_size, int max_blocks_per_seq, int num_blocks,
+                                    int max_seq_len, float scale, int partition_tokens,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_append_impl(nullptr, q, c_cache, c_new, block_table, seq_lens, batch, num_q_heads,
+                         d_c, d_rope, block_size, max_blocks_per_seq, num_blocks, max_seq_len,
+                         scale, partition_tokens, workspace, workspace_bytes, stream, false);
+}
+
+int decode_attn_mla_append(void* out, const void* q, void* c_cache, const void* c_new,
+                           const int32_t* block_table, const int32_t* seq_lens, int batch,
+                           int num_q_heads, int d_c, int d_rope, int block_size,
+                           int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                           int partition_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return mla_append_impl(out, q, c_cache, c_new, block_table, seq_lens, batch, num_q_heads, d_c,
+                         d_rope, block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale,
+                         partition_tokens, workspace, workspace_bytes, stream, true);
+}
+
 
 }  // extern "C"

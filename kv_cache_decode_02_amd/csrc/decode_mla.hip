@@ -109,6 +109,7 @@ struct MlaLaunchDev {
   int batch, num_heads, max_blocks_per_seq, num_blocks, max_seq_len;
   int partition_tokens, num_partitions, head_groups;
   float scale;
+  const uint16_t* c_new;    // fused append: [B, 576], NULL otherwise
 };
 
 __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) {
@@ -133,13 +134,20 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   const int p = pp % a.num_partitions;
   const int b = pp / a.num_partitions;
 
-  int len = a.seq_lens[b];
-  len = min(len, a.max_seq_len);
+  const int len_in = a.seq_lens[b];
+  int len = min(len_in, a.max_seq_len);
   len = min(len, a.max_blocks_per_seq * kBlockTokens);
   const int t_begin = p * a.partition_tokens;
   if (len <= t_begin) return;
   const int t_end = min(len, t_begin + a.partition_tokens);
   const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+  // Fused append: the partition holding position len - 1 takes that row from
+  // c_new (substituted when its tile is staged in LDS), and head group 0
+  // writes it into the cache slot.  Not for a length outside the bounds.
+  const bool fused = a.c_new != nullptr && len == len_in && t_end == len;
+  const int rel_new = len - 1 - t_begin;          // the new row in the partition
+  const int ti_new = fused ? rel_new / kTile : -1;  // its tile, -1 for none
+  const int r_new = rel_new % kBlockTokens;        // its row in its block
 
   const int head0 = hg * kHeadsPerGroup + hb * kHeadsPerWave;
   const bool active = head0 < a.num_heads;  // waves past the last head only load
@@ -181,6 +189,38 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   const int half = wave_uniform(wave >> 2);
   const int lt = tid & 255;
   uint32_t pre[2][kLoadWords];
+
+  // The new row's bytes in the lanes that load them from the cache block
+  // (load_tile's split of a block): at most one 16-byte chunk (c_sel) and
+  // one 8-byte piece (tail_sel) per lane.
+  int c_sel = -1;
+  bool tail_sel = false;
+  uint4 new16 = make_uint4(0u, 0u, 0u, 0u);
+  uint2 new8 = make_uint2(0u, 0u);
+  if (fused && half == ((rel_new / kBlockTokens) & 1)) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.c_new + static_cast<size_t>(b) * kW);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qi = lt + 256 * c;
+      if (qi / kChunks == r_new) {
+        c_sel = c;
+        new16 = *reinterpret_cast<const uint4*>(src + (qi % kChunks) * 16);
+      }
+    }
+    const int o = 4 * 256 * 16 + 8 * lt;
+    if (o / kRowBytes == r_new) {
+      tail_sel = true;
+      new8 = *reinterpret_cast<const uint2*>(src + o % kRowBytes);
+    }
+    const int jn = rel_new / kBlockTokens;  // block of the partition
+    if (hg == 0 && ((valid >> jn) & 1)) {
+      // The cache receives the caller's writable buffer on this path.
+      uint8_t* dst = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(a.cache)) +
+                     static_cast<size_t>(__builtin_amdgcn_readlane(entry, jn)) * kBlockTokens * kRowBytes;
+      if (c_sel >= 0) *reinterpret_cast<uint4*>(dst + (lt + 256 * c_sel) * 16) = new16;
+      if (tail_sel) *reinterpret_cast<uint2*>(dst + o) = new8;
+    }
+  }
   auto load_tile = [&](int ti, uint32_t (&dst)[kLoadWords]) __attribute__((always_inline)) {
     const int j = 2 * ti + half;  // block of the partition
     const int t0 = t_begin + j * kBlockTokens;
@@ -194,18 +234,23 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       buffer_load_words<4>(dst + 4 * c, r, static_cast<uint32_t>((lt + 256 * c) * 16));
     buffer_load_words<2>(dst + 16, r, static_cast<uint32_t>(4 * 256 * 16 + 8 * lt));
   };
-  auto store_tile = [&](const uint32_t (&src)[kLoadWords], uint8_t* tile)
+  // Tile tix goes to LDS; the tile holding the new row takes it from c_new.
+  auto store_tile = [&](const uint32_t (&src)[kLoadWords], uint8_t* tile, int tix)
       __attribute__((always_inline)) {
+    const bool sub = tix == ti_new;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int qi = lt + 256 * c;
       const int row = half * kBlockTokens + qi / kChunks, ch = qi % kChunks;
-      *reinterpret_cast<uint4*>(tile + row * kLdsRow + ch * 16) =
-          make_uint4(src[4 * c], src[4 * c + 1], src[4 * c + 2], src[4 * c + 3]);
+      uint4 v = make_uint4(src[4 * c], src[4 * c + 1], src[4 * c + 2], src[4 * c + 3]);
+      if (sub && c == c_sel) v = new16;
+      *reinterpret_cast<uint4*>(tile + row * kLdsRow + ch * 16) = v;
     }
     const int o = 4 * 256 * 16 + 8 * lt;
     const int row = half * kBlockTokens + o / kRowBytes;
-    *reinterpret_cast<uint2*>(tile + row * kLdsRow + o % kRowBytes) = make_uint2(src[16], src[17]);
+    uint2 t = make_uint2(src[16], src[17]);
+    if (sub && tail_sel) t = new8;
+    *reinterpret_cast<uint2*>(tile + row * kLdsRow + o % kRowBytes) = t;
   };
 
   // Valid rows of each 16-token half of tile ti (0 for a table entry outside
@@ -361,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) part[mt][i] = next[mt][i];
     }
-    store_tile(slot, tiles[nxt]);
+    store_tile(slot, tiles[nxt], ti + 2);
     load_tile(ti + 4, slot);
     __syncthreads();
     cur = nx;
@@ -369,8 +414,8 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
 
   load_tile(0, pre[0]);
   load_tile(1, pre[1]);
-  store_tile(pre[0], tiles[0]);
-  store_tile(pre[1], tiles[1]);
+  store_tile(pre[0], tiles[0], 0);
+  store_tile(pre[1], tiles[1], 1);
   load_tile(2, pre[0]);
   load_tile(3, pre[1]);
   __syncthreads();
@@ -425,6 +470,7 @@ hipError_t launch_mla_partials(const MlaLaunch& m, hipStream_t stream) {
   a.num_partitions = m.num_partitions;
   a.head_groups = mla_head_groups(m.num_heads);
   a.scale = m.scale;
+  a.c_new = static_cast<const uint16_t*>(m.c_new);
   // Workgroups come in runs of 8 (sequence, partition) pairs per head group.
   const long long pairs = static_cast<long long>(m.batch) * m.num_partitions;
   const long long groups = (pairs + 7) / 8 * 8 * a.head_groups;

@@ -137,6 +137,9 @@ struct MlaLaunch {
   int batch, num_heads, max_blocks_per_seq, num_blocks, max_seq_len;
   int partition_tokens, num_partitions;
   float scale;
+  // Fused append: this step's rows [B, d_c + d_rope] (NULL otherwise);
+  // c_cache is then written (the new rows' slots only).
+  const void* c_new;
 };
 
 // Each returns hipSuccess or the launch error.

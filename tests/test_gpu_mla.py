@@ -69,6 +69,66 @@ def test_mla_parity(name, c):
     log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")
 
 
+@pytest.mark.parametrize("name,c", CASES, ids=[n for n, _ in CASES])
+def test_mla_fused_append(name, c):
+    # decode_attn_mla_append = kv_append_paged + decode_attn_mla in one pass.
+    # The new slot holds the NaN sentinel before the call, so reading it
+    # instead of c_new would show.  Afterwards the cache equals the oracle's
+    # append bit for bit, and the output equals the two separate calls bit for
+    # bit (the row reaches the same LDS tile either way) and meets the
+    # contract against the oracle.
+    log(f"mla fused append {name}")
+    inp = make_mla(np.random.default_rng(zlib.crc32(name.encode()) + 1), c["B"], c["H"], 512, 64,
+                   c["lens"], std=c["std"])
+    fused, sep = Dev(inp), Dev(inp)
+    out = kvd.decode_attn_mla_append(fused.q, fused.c, fused.c_new[:, 0], fused.table, fused.seq,
+                                     inp.max_seq_len, partition_tokens=c["pt"])
+    torch.cuda.synchronize()
+    ref_cache, _ = oracle.append_paged(inp.c_pool, None, inp.c_new, None, inp.block_table,
+                                       inp.seq_lens)
+    assert np.array_equal(fused.c.cpu().view(torch.int16).numpy().view(np.uint16), ref_cache)
+    two = _step(sep, c["pt"])
+    assert torch.equal(out.view(torch.int16), two.view(torch.int16))
+    rep = assert_contract(down_f64(out), _ref(inp), name)
+    log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")
+
+
+def test_mla_fused_append_phases_and_skipped_last_block():
+    # The partials entry point with the merge equals the single call; a last
+    # block outside the pool is neither written nor read (its positions get
+    # no weight), as with the separate calls.
+    inp = make_mla(np.random.default_rng(5), 3, 64, 512, 64, [300, 33, 1000], std=1.0)
+    one_dev, two_dev = Dev(inp), Dev(inp)
+    one = kvd.decode_attn_mla_append(one_dev.q, one_dev.c, one_dev.c_new[:, 0], one_dev.table,
+                                     one_dev.seq, inp.max_seq_len, partition_tokens=256)
+    ws = kvd.alloc_workspace(3, 64, 1, 512, inp.max_seq_len, 256)
+    kvd.decode_attn_mla_append_partials(two_dev.q, two_dev.c, two_dev.c_new[:, 0], two_dev.table,
+                                        two_dev.seq, inp.max_seq_len, ws, partition_tokens=256)
+    two = torch.empty_like(one)
+    kvd.decode_attn_merge(two, two_dev.seq, 1, inp.max_seq_len, ws, partition_tokens=256)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    assert torch.equal(one_dev.c.view(torch.int16), two_dev.c.view(torch.int16))
+    # sequence 1 (33 positions): its third block (positions 32..) is outside the pool
+    dev = Dev(inp)
+    table = dev.table.clone()
+    table[1, 2] = inp.num_blocks + 7
+    before = dev.c.clone()
+    out = kvd.decode_attn_mla_append(dev.q, dev.c, dev.c_new[:, 0], table, dev.seq,
+                                     inp.max_seq_len, partition_tokens=256)
+    torch.cuda.synchronize()
+    got = down_f64(out)
+    scale = kvd.mla_default_scale()
+    C = oracle.to_f64(oracle.gather_logical(inp.c_pool, inp.block_table, 1, 32), "bf16")
+    assert_contract(got[1], oracle.mla_decode(oracle.to_f64(inp.q[1], "bf16"), C, 512, scale),
+                    "skipped last block")
+    # only the other two sequences' new slots changed
+    # (bitwise: the unfilled slots hold NaN)
+    changed = (dev.c.view(torch.int16) != before.view(torch.int16)).any(dim=-1).nonzero()
+    slots = {(int(inp.block_table[b, (n - 1) // 16]), (n - 1) % 16) for b, n in ((0, 300), (2, 1000))}
+    assert {(int(i), int(j)) for i, j in changed.cpu().numpy()} == slots
+
+
 def test_mla_scale_and_skipped_block():
     log("mla scale / bad entry")
     inp = make_mla(np.random.default_rng(3), 2, 32, 512, 64, [100, 100], std=1.0)
@@ -101,11 +161,17 @@ def test_mla_phases_equal_single_call():
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
-def test_mla_full_size_sampled():
-    log("mla full: generating")
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_mla_full_size_sampled(fused):
+    log(f"mla full ({'fused' if fused else 'separate'} append): generating")
     inp = make_config_inputs("mla_deepseek_v2")[0]
     dev = Dev(inp)
-    out = _step(dev)
+    if fused:
+        out = kvd.decode_attn_mla_append(dev.q, dev.c, dev.c_new[:, 0], dev.table, dev.seq,
+                                         inp.max_seq_len)
+        torch.cuda.synchronize()
+    else:
+        out = _step(dev)
     got = down_f64(out)
     assert np.all(np.isfinite(got))
     scale = kvd.mla_default_scale()

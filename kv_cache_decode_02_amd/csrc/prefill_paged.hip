@@ -70,7 +70,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillLaunch a) {
   constexpr int KS = D / 32;           // score K-steps
   constexpr int NT = D / 16;           // output tiles over D
   constexpr int RB = D * 2;            // bytes of one token row of one head
-  constexpr int LROW = RB + 16;        // padded LDS row
+  // Padded LDS row: 32 bytes of padding spread both the 16-byte score reads
+  // (16 rows apart) and the 8-byte transpose reads (4 consecutive rows) over
+  // distinct banks; with 16 bytes the transpose reads conflicted (0.44 bank
+  // conflicts per LDS access, 0 with 32).
+  constexpr int LROW = RB + 32;
   constexpr int CPT = RB / 16;         // 16-byte chunks per token row
   constexpr int CHUNKS = kPTile * CPT;  // 16-byte chunks per tile and tensor
   constexpr int LOADS = (CHUNKS + kPThreads - 1) / kPThreads;  // per thread

@@ -86,3 +86,36 @@ def test_non_finite_query_is_refused(validating):
     q[1, 3, 5] = float("nan")
     with pytest.raises(kvd.KvdError):
         kvd.decode_attn_paged(q, dev.k_cache, dev.v_cache, dev.table, dev.seq, inp.max_seq_len)
+
+
+def test_mla_fused_append_checks(validating):
+    # The fused MLA append: a valid call gives the same bits as without the
+    # checks; a non-finite new latent row, or a new row that lands in a block
+    # another sequence also reads, is refused and the cache stays untouched.
+    log("validate: fused MLA append")
+    from workloads import make_mla
+    from gpu_util import up
+    inp = make_mla(np.random.default_rng(22), 2, 16, 512, 64, [40, 100], std=1.0)
+    q, table, seq = up(inp.q), up(inp.block_table), up(inp.seq_lens)
+    c_new = up(inp.c_new)
+    c1, c2 = up(inp.c_pool), up(inp.c_pool)
+    checked = kvd.decode_attn_mla_append(q, c1, c_new, table, seq, inp.max_seq_len)
+    torch.cuda.synchronize()
+    del os.environ["KVD_VALIDATE"]
+    plain = kvd.decode_attn_mla_append(q, c2, c_new, table, seq, inp.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(checked.view(torch.int16), plain.view(torch.int16))
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+    os.environ["KVD_VALIDATE"] = "1"
+    fresh = up(inp.c_pool)
+    before = fresh.clone()
+    bad_row = c_new.clone()
+    bad_row[1, 7] = float("inf")
+    with pytest.raises(kvd.KvdError):
+        kvd.decode_attn_mla_append(q, fresh, bad_row, table, seq, inp.max_seq_len)
+    shared = table.clone()
+    shared[0, 2] = shared[1, 3]      # sequence 0's last block is one sequence 1 reads
+    with pytest.raises(kvd.KvdError):
+        kvd.decode_attn_mla_append(q, fresh, c_new, shared, seq, inp.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(fresh.view(torch.int16), before.view(torch.int16))

@@ -51,8 +51,11 @@ constexpr int kMinPieceBlocks = kBalancedMinPieceBlocks;
 constexpr long long kEvenXcdShare = 1120;
 constexpr long long kOddXcdShare = 1000;
 // Virtual blocks charged for each segment (sequence, unit group) a share
-// starts: the restart of the load pipeline costs about one block's time.
-constexpr int kSegmentCost = 1;
+// starts: the restart (query and block-id loads, then the first blocks'
+// loads) costs a few blocks' time.  Measured on MI355X with the GQA decode
+// batch over 0 .. 6: shortest at 3 - 4 (1.3% below 1), the MHA batch
+// unchanged.
+constexpr int kSegmentCost = 4;
 
 template <int KT, int D>
 struct RowShape {

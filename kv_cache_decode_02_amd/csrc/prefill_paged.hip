@@ -12,15 +12,18 @@
 // Work decomposition: a workgroup of 8 waves takes 128 "rows" of one (sequence,
 // KV head g): row rho = (token t of the chunk, head hh of the group) with
 // rho = t * r + hh, so the r query heads that share g's K/V are rows of the
-// same tiles.  K/V stream through LDS in 32-token tiles (two 16-token blocks,
-// double-buffered); every wave reads them for its 16 rows.
-//   Scores: S^T[token][row] = K_tile[32 x D] . Q^T[D x 16], 2 x D/32 MFMA
+// same tiles.  K/V stream through LDS in 64-token tiles (four 16-token blocks,
+// double-buffered); every wave reads them for its 16 rows.  (64 tokens rather
+// than 32: twice the independent score accumulators and half the barriers
+// and softmax passes per token, 3% faster on MI355X.)
+//   Scores: S^T[token][row] = K_tile[64 x D] . Q^T[D x 16], 4 x D/32 MFMA
 //           16x16x32 bf16 per wave and tile; Q^T stays in registers (B).
-//           Each lane ends with one row and 8 tokens.
+//           Each lane ends with one row and 16 tokens.
 //   Softmax: online per row with a lazily raised reference max (log2 units);
 //           the mask drops tokens past the row's position.
-//   Values: O^T[D x 16] += V_tile^T[D x 32] . P^T[32 x 16]; V^T comes from the
-//           token-major tile by LDS transpose loads.  The weights enter as a
+//   Values: O^T[D x 16] += V_tile^T[D x 32] . P^T[32 x 16] for each 32-token
+//           half of the tile; V^T comes from the token-major tile by LDS
+//           transpose loads.  The weights enter as a
 //           bf16 high part and a bf16 remainder (two MFMAs), about 16 bits of
 //           weight, since rows over a few positions cancel to small outputs
 //           that 8-bit weights would move by ~1e-3; the sum takes the fp32
@@ -31,7 +34,7 @@
 namespace kvd {
 namespace {
 
-constexpr int kPTile = 32;        // tokens per K/V tile
+constexpr int kPTile = 64;        // tokens per K/V tile
 constexpr int kPWaves = 8;
 constexpr int kPRows = 16 * kPWaves;  // rows per workgroup (16 per wave)
 constexpr int kPThreads = 64 * kPWaves;
@@ -168,22 +171,25 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillLaunch a) {
   };
 
   auto compute = [&](int ti, int buf) __attribute__((always_inline)) {
+    constexpr int MT = kPTile / 16;   // 16-token score blocks per tile
     // Scores: lane gets row col, tokens 16 mt + 4 kb + i of the tile.
-    pf32x4_t s[2] = {pf32x4_t{0.f, 0.f, 0.f, 0.f}, pf32x4_t{0.f, 0.f, 0.f, 0.f}};
+    pf32x4_t s[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) s[mt] = pf32x4_t{0.f, 0.f, 0.f, 0.f};
     const uint8_t* arow = &ktile[buf][col * LROW + 16 * kb];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const pbf16x8_t bq = pas_bf16x8(qf[ks][0], qf[ks][1], qf[ks][2], qf[ks][3]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const uint4 av = *reinterpret_cast<const uint4*>(arow + 16 * mt * LROW + 64 * ks);
         s[mt] = pmfma16(pas_bf16x8(av.x, av.y, av.z, av.w), bq, s[mt]);
       }
     }
-    float z[2][4];
+    float z[MT][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tp = kPTile * ti + 16 * mt + 4 * kb + i;
@@ -202,35 +208,36 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillLaunch a) {
         for (int i = 0; i < 4; ++i) acc[nt][i] *= alpha;
       m_run = mn;
     }
-    // Weights as B: K-slot j < 4 is token 4 kb + j, j >= 4 token 16 + 4 kb +
-    // (j - 4); high bf16 parts and the bf16 remainders.
-    uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int hh = 0; hh < MT / 2; ++hh) {
+      // Weights as B for the 32 tokens 32 hh ..: K-slot j < 4 is token 4 kb +
+      // j, j >= 4 token 16 + 4 kb + (j - 4); high bf16 parts and remainders.
+      uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const float p0 = exp2_fast(z[mt][2 * pr] - m_run);
-        const float p1 = exp2_fast(z[mt][2 * pr + 1] - m_run);
-        l_lane += p0 + p1;
-        const uint32_t h = pack_bf16x2(p0, p1);
-        hi[2 * mt + pr] = h;
-        lo[2 * mt + pr] = pack_bf16x2(p0 - bf16_lo(h), p1 - bf16_hi(h));
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const float p0 = exp2_fast(z[2 * hh + m2][2 * pr] - m_run);
+          const float p1 = exp2_fast(z[2 * hh + m2][2 * pr + 1] - m_run);
+          l_lane += p0 + p1;
+          const uint32_t h = pack_bf16x2(p0, p1);
+          hi[2 * m2 + pr] = h;
+          lo[2 * m2 + pr] = pack_bf16x2(p0 - bf16_lo(h), p1 - bf16_hi(h));
+        }
+      const pbf16x8_t phi = pas_bf16x8(hi[0], hi[1], hi[2], hi[3]);
+      const pbf16x8_t plo = pas_bf16x8(lo[0], lo[1], lo[2], lo[3]);
+      const uint8_t* vrow0 = &vtile[buf][(32 * hh + 4 * kb + (col >> 2)) * LROW + 8 * (col & 3)];
+      const uint8_t* vrow1 = vrow0 + 16 * LROW;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const ps16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((plds_s16x4_t*)(vrow0 + 32 * nt));
+        const ps16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((plds_s16x4_t*)(vrow1 + 32 * nt));
+        const uint2 w0 = __builtin_bit_cast(uint2, v0);
+        const uint2 w1 = __builtin_bit_cast(uint2, v1);
+        const pbf16x8_t av = pas_bf16x8(w0.x, w0.y, w1.x, w1.y);
+        acc[nt] = pmfma16(av, phi, acc[nt]);
+        acc[nt] = pmfma16(av, plo, acc[nt]);
       }
-    const pbf16x8_t phi = pas_bf16x8(hi[0], hi[1], hi[2], hi[3]);
-    const pbf16x8_t plo = pas_bf16x8(lo[0], lo[1], lo[2], lo[3]);
-    // Values as A by LDS transpose loads: lane (col, kb) ends with tokens
-    // 4 kb .. +3 (v0) and 16 + 4 kb .. +3 (v1) of dimension 16 nt + col.
-    const uint8_t* vrow0 = &vtile[buf][(4 * kb + (col >> 2)) * LROW + 8 * (col & 3)];
-    const uint8_t* vrow1 = vrow0 + 16 * LROW;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const ps16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((plds_s16x4_t*)(vrow0 + 32 * nt));
-      const ps16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((plds_s16x4_t*)(vrow1 + 32 * nt));
-      const uint2 w0 = __builtin_bit_cast(uint2, v0);
-      const uint2 w1 = __builtin_bit_cast(uint2, v1);
-      const pbf16x8_t av = pas_bf16x8(w0.x, w0.y, w1.x, w1.y);
-      acc[nt] = pmfma16(av, phi, acc[nt]);
-      acc[nt] = pmfma16(av, plo, acc[nt]);
     }
   };
 

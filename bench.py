@@ -589,7 +589,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence or KV head with no exchange; see DESIGN.md)",
+              "(the decode path would shard by sequence or KV head, with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

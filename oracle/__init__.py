@@ -47,13 +47,11 @@ from .attention import (
 )
 from .quant import (
     quantize,
-    token_scale,
     channel_scales,
     append_paged_int8,
     dequantize_k,
     dequantize_v,
     decode_attn_paged_int8,
-    history_int8,
 )
 from .quant_fp8 import (
     e4m3_value,
@@ -82,8 +80,8 @@ __all__ = [
     "mla_decode", "mla_decode_paged", "causal_attention", "prefill_attn_paged",
     "bytes_per_token", "paged_capacity", "unique_block_bytes",
     "kv_cache_bytes", "mla_elements_per_token",
-    "quantize", "token_scale", "channel_scales", "append_paged_int8", "dequantize_k",
-    "dequantize_v", "decode_attn_paged_int8", "history_int8",
+    "quantize", "channel_scales", "append_paged_int8", "dequantize_k",
+    "dequantize_v", "decode_attn_paged_int8",
     "e4m3_value", "e4m3_decode", "e4m3_encode", "quantize_fp8", "channel_scales_fp8",
     "append_paged_fp8", "decode_attn_paged_fp8",
     "block_hashes", "BlockPool", "PoolExhausted",

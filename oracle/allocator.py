@@ -18,7 +18,11 @@ Citation keys are listed in ``oracle/__init__.py``.
 
 The model mirrors the library's policy (blocks never keyed are reused
 first, then keyed ones in release order), so tests can compare block ids
-exactly; the properties above are also checked on their own.
+exactly.  That comparison is not independent of the policy; the pin that is
+simulates the pool's memory contents (copy pairs applied, new tokens written
+through the tables) and checks that every sequence reads back exactly its
+own tokens, that written blocks are held by one sequence, that counts equal
+table occurrences and that use equals the unique blocks in the tables.
 """
 
 import hashlib

@@ -47,12 +47,6 @@ def quantize(x, s):
     return q.astype(np.int8)
 
 
-def token_scale(row):
-    """Per-token scale of one fp32 row: max |v| / 127 in fp32."""
-    row = np.asarray(row, dtype=np.float32)
-    return np.float32(np.max(np.abs(row))) / np.float32(CODE_MAX)
-
-
 def channel_scales(K):
     """Per-channel K scales from a calibration set K [T, H_kv, d]: max over
     the tokens of |K| / 127 per (head, dimension), fp32."""
@@ -132,10 +126,3 @@ def decode_attn_paged_int8(q, kq_pool, vq_pool, vs_pool, k_scale, block_table, s
         outs.append(decode_attention(to_f64(q[b], dtype), K, V, scale))
     return np.stack(outs)
 
-
-def history_int8(kq_pool, vq_pool, vs_pool, k_scale, block_table, seq_lens, b, block_size=16):
-    """Dequantised history (positions < seq_lens[b] - 1) of sequence b."""
-    K = dequantize_k(gather_history(kq_pool, block_table, seq_lens, b, block_size), k_scale)
-    V = dequantize_v(gather_history(vq_pool, block_table, seq_lens, b, block_size),
-                     gather_history(vs_pool, block_table, seq_lens, b, block_size))
-    return K, V

@@ -164,3 +164,74 @@ def test_random_operations_match_the_model():
             assert lib.available() == ref.available() and lib.used() == ref.used()
             assert [lib.ref(b) for b in range(nb)] == ref.ref
         lib.close()
+
+
+def test_random_operations_keep_every_sequence_s_own_tokens():
+    # Independent of the reuse order: simulate the pool's memory, apply each
+    # append's copy pairs and then write the new tokens through the table, as
+    # the device would.  Every live sequence must then read back exactly its
+    # own token history; a block that one sequence writes is held by it alone
+    # ([DQ] 08 PagedAttention, copy-on-write of shared pages; [LC] 2.3);
+    # counts equal the number of tables that hold a block; physical use is the
+    # number of unique blocks in the tables ([SW] 源码导读); a prefix hit
+    # hands out blocks whose contents are the tokens the keys were made from
+    # ([SW] 知识点三).
+    rng = np.random.default_rng(12)
+    serial = iter(range(1, 1 << 30))
+    for trial in range(20):
+        nb, bs = int(rng.integers(4, 40)), int(rng.choice([1, 2, 16]))
+        pool = kvd.BlockPool(nb, bs)
+        mem = np.full((nb, bs), -1, dtype=np.int64)
+        hist = {}  # sequence -> its logical tokens
+        for _ in range(200):
+            op = rng.integers(0, 6)
+            live = sorted(hist)
+            if op == 0 or not live:
+                hist[pool.create()] = []
+            elif op == 1:
+                s = int(rng.choice(live))
+                hist[pool.fork(s)] = list(hist[s])
+            elif op == 2 and len(live) > 1:
+                s = int(rng.choice(live))
+                pool.release(s)
+                del hist[s]
+            elif op in (3, 4):
+                s = int(rng.choice(live))
+                n = int(rng.integers(0, 3 * bs))
+                before = {t: list(pool.table(t)) for t in hist}
+                try:
+                    copies = pool.append(s, n)
+                except kvd.PoolExhausted:
+                    assert {t: pool.table(t) for t in hist} == before
+                    continue
+                held = {b for t in before for b in before[t]}
+                for old, new in copies:
+                    assert old in before[s] and new not in held
+                    mem[new] = mem[old]
+                toks = [next(serial) for _ in range(n)]
+                table = pool.table(s)
+                start = len(hist[s])
+                for i, tok in enumerate(toks):
+                    blk = table[(start + i) // bs]
+                    # the written block belongs to s alone
+                    assert sum(blk in pool.table(t) for t in hist) == 1
+                    mem[blk, (start + i) % bs] = tok
+                hist[s] += toks
+            else:
+                s = int(rng.choice(live))
+                full = len(hist[s]) // bs
+                keys = kvd.block_hashes(hist[s][:full * bs], bs, b"t")
+                pool.commit(s, keys)
+                s2, hit = pool.create_with_prefix(keys)
+                hist[s2] = list(hist[s][:hit * bs])
+            for t, toks in hist.items():
+                table = pool.table(t)
+                assert pool.length(t) == len(toks)
+                assert len(table) == -(-len(toks) // bs)
+                got = [int(mem[table[i // bs], i % bs]) for i in range(len(toks))]
+                assert got == toks, (trial, t)
+            tables = [pool.table(t) for t in hist]
+            for b in range(nb):
+                assert pool.ref(b) == sum(tbl.count(b) for tbl in tables)
+            assert pool.used() == len({b for tbl in tables for b in tbl})
+        pool.close()

@@ -38,7 +38,8 @@ FP8 caches (``make_paged_decode_fp8``) hold E4M3 bytes: a uniform sign and a
 magnitude code uniform in 0x00 .. 0x3F (the values 0 .. 1.875, from 2^-9 up
 through the subnormals and eight binades), K and V scales uniform in
 std * [0.5, 1.5], so that the cached values again have roughly the spread of
-the bf16 workloads.  Unfilled slots hold code 0x7F (E4M3 NaN, never written
+the bf16 workloads.  With ``full_range`` the magnitude codes cover every
+finite value 0x00 .. 0x7E (up to 448) and the scales are std * [0.5, 1.5] / 256.  Unfilled slots hold code 0x7F (E4M3 NaN, never written
 by the append) and a NaN V scale in parity runs, code 0 and scale 0 in timing
 runs.  Same draw order as the INT8 caches.
 """
@@ -316,20 +317,29 @@ def make_paged_decode_int8(rng, B, H_q, H_kv, d, seq_lens, table="permuted", std
                            vs, ks, k_new, v_new)
 
 
-def _fp8_codes(rng, shape):
+def _fp8_codes(rng, shape, full_range=False):
+    """E4M3 bytes with a uniform sign bit.  Magnitude codes uniform in
+    0x00 .. 0x3F, or with ``full_range`` in 0x00 .. 0x7E (every finite
+    magnitude, up to 448; 0x7F is NaN and is never drawn)."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint8)
     for start in range(0, n, _CHUNK):
         stop = min(start + _CHUNK, n)
-        out[start:stop] = rng.integers(0, 0x80, size=stop - start, dtype=np.uint8)
-    # bit 7: sign; bits 0-5: magnitude code 0x00 .. 0x3F (bit 6 cleared)
-    return (out & np.uint8(0xBF)).reshape(shape)
+        if full_range:
+            v = rng.integers(0, 254, size=stop - start, dtype=np.int32)
+            out[start:stop] = ((v % 127) | ((v // 127) << 7)).astype(np.uint8)
+        else:
+            v = rng.integers(0, 256, size=stop - start, dtype=np.int32).astype(np.uint8)
+            out[start:stop] = v & np.uint8(0xBF)  # bit 7 sign, bit 6 cleared
+    return out.reshape(shape)
 
 
 def make_paged_decode_fp8(rng, B, H_q, H_kv, d, seq_lens, table="permuted", std=1.0,
-                          sentinel="nan", max_blocks_per_seq=None, block_size=BLOCK_SIZE):
+                          sentinel="nan", max_blocks_per_seq=None, block_size=BLOCK_SIZE,
+                          full_range=False):
     """Draw one decode step's inputs over an FP8 (E4M3) cache (see the module
-    docstring)."""
+    docstring).  ``full_range``: history codes over every finite magnitude
+    (0x00 .. 0x7E) with scales std * [0.5, 1.5] / 256."""
     lens = np.asarray(seq_lens, dtype=np.int64)
     if lens.shape != (B,) or np.any(lens < 1):
         raise ValueError("seq_lens must have B entries, each >= 1")
@@ -338,10 +348,11 @@ def make_paged_decode_fp8(rng, B, H_q, H_kv, d, seq_lens, table="permuted", std=
     mb = max_blocks_per_seq or _blocks_needed(lens.max(), block_size)
     bt, nb, owned = _assign_blocks(rng, lens, block_size, mb, table)
     q = _draw(rng, (B, H_q, d), std, "bf16")
-    kq = _fp8_codes(rng, (nb, block_size, H_kv, d))
-    vq = _fp8_codes(rng, (nb, block_size, H_kv, d))
-    vs = _scales(rng, (nb, block_size, H_kv), std * 64.0)
-    ks = _scales(rng, (H_kv, d), std * 64.0)
+    kq = _fp8_codes(rng, (nb, block_size, H_kv, d), full_range)
+    vq = _fp8_codes(rng, (nb, block_size, H_kv, d), full_range)
+    sstd = std / 4.0 if full_range else std * 64.0
+    vs = _scales(rng, (nb, block_size, H_kv), sstd)
+    ks = _scales(rng, (H_kv, d), sstd)
     k_new = _draw(rng, (B, H_kv, d), std, "bf16")
     v_new = _draw(rng, (B, H_kv, d), std, "bf16")
     if sentinel == "nan":

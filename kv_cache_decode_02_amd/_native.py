@@ -151,15 +151,38 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _need(t, name, device=True, dtype=None, contiguous=True):
+def _need(t, name, device=True, dtype=None, contiguous=True, like=None):
+    """Device, dtype and contiguity of an argument; ``like``: a tensor whose
+    device it must share."""
     if t is None:
         raise KvdError(f"{name} is required")
     if device and not t.is_cuda:
         raise KvdError(f"{name} must be a device tensor")
+    if like is not None and t.device != like.device:
+        raise KvdError(f"{name} must be on {like.device} (is on {t.device})")
     if dtype is not None and t.dtype != dtype:
         raise KvdError(f"{name} must be {dtype}")
     if contiguous and not t.is_contiguous():
         raise KvdError(f"{name} must be contiguous")
+
+
+# Shape checks run before anything else (before the device checks too): a
+# kernel indexes every argument from the sizes of the others, so a short
+# seq_lens, block table or output would be read or written past its end.
+def _dims(t, name, shape):
+    """``t`` has len(shape) dimensions with the given sizes (None: any)."""
+    if t is None:
+        raise KvdError(f"{name} is required")
+    if t.dim() != len(shape) or any(w is not None and int(w) != int(n)
+                                    for w, n in zip(shape, t.shape)):
+        want = ", ".join("*" if w is None else str(int(w)) for w in shape)
+        raise KvdError(f"{name} must be [{want}], got {list(t.shape)}")
+
+
+def _batch(seq_lens, block_table, B):
+    """seq_lens [B] and block_table [B, max_blocks_per_seq]."""
+    _dims(seq_lens, "seq_lens", (B,))
+    _dims(block_table, "block_table", (B, None))
 
 
 def kv_append_paged(k_cache, v_cache, k_new, v_new, block_table, seq_lens, stream=None):
@@ -168,13 +191,23 @@ def kv_append_paged(k_cache, v_cache, k_new, v_new, block_table, seq_lens, strea
     k_cache/v_cache: [num_blocks, 16, H_kv, d]; k_new/v_new: [B, H_kv, d];
     v_cache and v_new may both be None (latent cache).
     """
-    for t, n in ((k_cache, "k_cache"), (k_new, "k_new"), (block_table, "block_table"),
-                 (seq_lens, "seq_lens")):
-        _need(t, n)
-    _need(block_table, "block_table", dtype=torch.int32)
-    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    _dims(k_cache, "k_cache", (None,) * 4)
     nb, bs, h_kv, d = k_cache.shape
+    _dims(k_new, "k_new", (None, h_kv, d))
     B = k_new.shape[0]
+    _batch(seq_lens, block_table, B)
+    if (v_cache is None) != (v_new is None):
+        raise KvdError("v_cache and v_new must both be given or both be None")
+    if v_cache is not None:
+        _dims(v_cache, "v_cache", tuple(k_cache.shape))
+        _dims(v_new, "v_new", tuple(k_new.shape))
+    _need(k_cache, "k_cache")
+    _need(k_new, "k_new", dtype=k_cache.dtype, like=k_cache)
+    if v_cache is not None:
+        _need(v_cache, "v_cache", dtype=k_cache.dtype, like=k_cache)
+        _need(v_new, "v_new", dtype=k_cache.dtype, like=k_cache)
+    _need(block_table, "block_table", dtype=torch.int32, like=k_cache)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, like=k_cache)
     status = lib.kv_append_paged(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                                  _ptr(block_table), _ptr(seq_lens), B, h_kv, d, bs,
                                  block_table.shape[1], nb, _dtype_code(k_cache), _stream(stream))
@@ -207,16 +240,20 @@ def alloc_workspace(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, par
 
 
 def _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
-                partition_tokens, ws):
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
-                 (block_table, "block_table"), (seq_lens, "seq_lens"), (ws, "workspace")):
-        _need(t, n)
-    _need(block_table, "block_table", dtype=torch.int32)
-    _need(seq_lens, "seq_lens", dtype=torch.int32)
+                partition_tokens, ws, out=None):
+    _dims(q, "q", (None,) * 3)
     B, h_q, d = q.shape
-    nb, bs, h_kv, d2 = k_cache.shape
-    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise KvdError("q, k_cache and v_cache head sizes disagree")
+    _dims(k_cache, "k_cache", (None, None, None, d))
+    _dims(v_cache, "v_cache", tuple(k_cache.shape))
+    nb, bs, h_kv, _ = k_cache.shape
+    _batch(seq_lens, block_table, B)
+    if out is not None:
+        _dims(out, "out", (B, h_q, d))
+        _need(out, "out", dtype=q.dtype, like=q)
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (ws, "workspace")):
+        _need(t, n, like=q)
+    _need(block_table, "block_table", dtype=torch.int32, like=q)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, like=q)
     if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
         raise KvdError("q, k_cache and v_cache must share one dtype")
     if scale is None:
@@ -229,6 +266,8 @@ def _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
 def decode_attn_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=None,
                       partition_tokens=0, workspace=None, out=None, stream=None):
     """Decode attention of q [B, H_q, d] over the paged K/V caches; returns out."""
+    _dims(q, "q", (None,) * 3)
+    _dims(k_cache, "k_cache", (None,) * 4)
     B, h_q, d = q.shape
     h_kv = k_cache.shape[2]
     if workspace is None:
@@ -236,9 +275,8 @@ def decode_attn_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, s
                                     device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=q.dtype)
     args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
-                       partition_tokens, workspace)
+                       partition_tokens, workspace, out)
     _check(lib.decode_attn_paged(_ptr(out), *args, _stream(stream)), "decode_attn_paged")
     return out
 
@@ -256,6 +294,8 @@ def decode_attn_paged_window(q, k_cache, v_cache, block_table, seq_lens, max_seq
                              stream=None):
     """decode_attn_paged under a sliding window: each row attends to its
     last ``window`` positions; returns out."""
+    _dims(q, "q", (None,) * 3)
+    _dims(k_cache, "k_cache", (None,) * 4)
     B, h_q, d = q.shape
     h_kv = k_cache.shape[2]
     if workspace is None:
@@ -263,9 +303,8 @@ def decode_attn_paged_window(q, k_cache, v_cache, block_table, seq_lens, max_seq
                                     device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=q.dtype)
     args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
-                       partition_tokens, workspace)
+                       partition_tokens, workspace, out)
     args = args[:14] + [int(window)] + args[14:]
     _check(lib.decode_attn_paged_window(_ptr(out), *args, _stream(stream)),
            "decode_attn_paged_window")
@@ -284,13 +323,15 @@ def decode_attn_paged_window_partials(q, k_cache, v_cache, block_table, seq_lens
 
 
 def _append_args(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens, max_seq_len, scale,
-                 partition_tokens, ws):
-    args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
-                       partition_tokens, ws)
+                 partition_tokens, ws, out=None):
+    _dims(q, "q", (None,) * 3)
+    _dims(k_cache, "k_cache", (None, None, None, q.shape[2]))
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
-        _need(t, n, dtype=k_cache.dtype)
-        if tuple(t.shape) != (q.shape[0], k_cache.shape[2], k_cache.shape[3]):
-            raise KvdError(f"{n} must be [B, H_kv, d]")
+        _dims(t, n, (q.shape[0], k_cache.shape[2], k_cache.shape[3]))
+    args = _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+                       partition_tokens, ws, out)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, dtype=k_cache.dtype, like=q)
     return args[:3] + [_ptr(k_new), _ptr(v_new)] + args[3:]
 
 
@@ -299,6 +340,8 @@ def decode_attn_paged_append(q, k_cache, v_cache, k_new, v_new, block_table, seq
                              out=None, stream=None):
     """kv_append_paged + decode_attn_paged in one pass: writes k_new / v_new
     [B, H_kv, d] into their slots and attends over the history plus them."""
+    _dims(q, "q", (None,) * 3)
+    _dims(k_cache, "k_cache", (None,) * 4)
     B, h_q, d = q.shape
     h_kv = k_cache.shape[2]
     if workspace is None:
@@ -306,9 +349,8 @@ def decode_attn_paged_append(q, k_cache, v_cache, k_new, v_new, block_table, seq
                                     device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=q.dtype)
     args = _append_args(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens, max_seq_len,
-                        scale, partition_tokens, workspace)
+                        scale, partition_tokens, workspace, out)
     _check(lib.decode_attn_paged_append(_ptr(out), *args, _stream(stream)),
            "decode_attn_paged_append")
     return out
@@ -327,10 +369,12 @@ def decode_attn_paged_append_partials(q, k_cache, v_cache, k_new, v_new, block_t
 def decode_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_tokens=0,
                       stream=None):
     """Second phase only: merges the partials in ``workspace`` into ``out``."""
-    _need(out, "out")
-    _need(seq_lens, "seq_lens", dtype=torch.int32)
-    _need(workspace, "workspace")
+    _dims(out, "out", (None,) * 3)
     B, h_q, d = out.shape
+    _dims(seq_lens, "seq_lens", (B,))
+    _need(out, "out")
+    _need(seq_lens, "seq_lens", dtype=torch.int32, like=out)
+    _need(workspace, "workspace", like=out)
     status = lib.decode_attn_merge(_ptr(out), _ptr(seq_lens), B, h_q, num_kv_heads, d,
                                    int(max_seq_len), int(partition_tokens), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(),
@@ -347,18 +391,24 @@ def mla_default_scale(d_c=MLA_D_C, d_rope=MLA_D_ROPE):
     return 1.0 / math.sqrt(d_c // 4 + d_rope)
 
 
-def _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale, partition_tokens, ws):
-    for t, n in ((q, "q"), (c_cache, "c_cache"), (block_table, "block_table"),
-                 (seq_lens, "seq_lens"), (ws, "workspace")):
-        _need(t, n)
-    _need(q, "q", dtype=torch.bfloat16)
-    _need(c_cache, "c_cache", dtype=torch.bfloat16)
-    _need(block_table, "block_table", dtype=torch.int32)
-    _need(seq_lens, "seq_lens", dtype=torch.int32)
+def _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale, partition_tokens, ws,
+              out=None):
+    _dims(q, "q", (None,) * 3)
     B, h, w = q.shape
+    if c_cache is None or c_cache.dim() < 3:
+        raise KvdError("c_cache must be [num_blocks, 16, d_c + d_rope]")
     nb, bs = c_cache.shape[0], c_cache.shape[1]
     if c_cache.shape[-1] != w or c_cache.numel() != nb * bs * w:
         raise KvdError("c_cache must be [num_blocks, 16, d_c + d_rope] like q's rows")
+    _batch(seq_lens, block_table, B)
+    if out is not None:
+        _dims(out, "out", (B, h, d_c))
+        _need(out, "out", dtype=torch.bfloat16, like=q)
+    _need(q, "q", dtype=torch.bfloat16)
+    _need(c_cache, "c_cache", dtype=torch.bfloat16, like=q)
+    _need(ws, "workspace", like=q)
+    _need(block_table, "block_table", dtype=torch.int32, like=q)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, like=q)
     if scale is None:
         scale = mla_default_scale(d_c, w - d_c)
     return [_ptr(q), _ptr(c_cache), _ptr(block_table), _ptr(seq_lens), B, h, d_c, w - d_c, bs,
@@ -370,14 +420,14 @@ def decode_attn_mla(q, c_cache, block_table, seq_lens, max_seq_len, d_c=MLA_D_C,
                     partition_tokens=0, workspace=None, out=None, stream=None):
     """Absorbed-MLA decode of q [B, H, d_c + d_rope] over the latent cache; returns
     out [B, H, d_c] (bf16)."""
+    _dims(q, "q", (None,) * 3)
     B, h, _ = q.shape
     if workspace is None:
         workspace = alloc_workspace(B, h, 1, d_c, max_seq_len, partition_tokens, device=q.device)
     if out is None:
         out = torch.empty((B, h, d_c), dtype=torch.bfloat16, device=q.device)
-    _need(out, "out", dtype=torch.bfloat16)
     args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
-                     partition_tokens, workspace)
+                     partition_tokens, workspace, out)
     _check(lib.decode_attn_mla(_ptr(out), *args, _stream(stream)), "decode_attn_mla")
     return out
 
@@ -391,12 +441,13 @@ def decode_attn_mla_partials(q, c_cache, block_table, seq_lens, max_seq_len, wor
 
 
 def _mla_append_args(q, c_cache, c_new, block_table, seq_lens, max_seq_len, d_c, scale,
-                     partition_tokens, ws):
-    args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
-                     partition_tokens, ws)
-    _need(c_new, "c_new", dtype=torch.bfloat16)
-    if c_new.numel() != q.shape[0] * q.shape[2]:
+                     partition_tokens, ws, out=None):
+    if c_new is None or c_new.dim() < 2 or c_new.shape[0] != q.shape[0] or \
+            c_new.numel() != q.shape[0] * q.shape[2]:
         raise KvdError("c_new must be [B, d_c + d_rope] (one latent row per sequence)")
+    args = _mla_args(q, c_cache, block_table, seq_lens, max_seq_len, d_c, scale,
+                     partition_tokens, ws, out)
+    _need(c_new, "c_new", dtype=torch.bfloat16, like=q)
     return args[:2] + [_ptr(c_new)] + args[2:]
 
 
@@ -405,14 +456,14 @@ def decode_attn_mla_append(q, c_cache, c_new, block_table, seq_lens, max_seq_len
                            stream=None):
     """kv_append_paged of c_new [B, d_c + d_rope] + decode_attn_mla in one pass:
     writes each row into its slot and attends over the history plus it."""
+    _dims(q, "q", (None,) * 3)
     B, h, _ = q.shape
     if workspace is None:
         workspace = alloc_workspace(B, h, 1, d_c, max_seq_len, partition_tokens, device=q.device)
     if out is None:
         out = torch.empty((B, h, d_c), dtype=torch.bfloat16, device=q.device)
-    _need(out, "out", dtype=torch.bfloat16)
     args = _mla_append_args(q, c_cache, c_new, block_table, seq_lens, max_seq_len, d_c, scale,
-                            partition_tokens, workspace)
+                            partition_tokens, workspace, out)
     _check(lib.decode_attn_mla_append(_ptr(out), *args, _stream(stream)), "decode_attn_mla_append")
     return out
 
@@ -452,22 +503,23 @@ def kv_append_paged_fp8(k_cache, v_cache, v_scale, k_new, v_new, k_scale, block_
 
 def _append_bytes(name, code_dtype, k_cache, v_cache, v_scale, k_new, v_new, k_scale,
                   block_table, seq_lens, stream):
-    _need(k_cache, "k_cache", dtype=code_dtype)
-    _need(v_cache, "v_cache", dtype=code_dtype)
-    _need(v_scale, "v_scale", dtype=torch.float32)
-    _need(k_scale, "k_scale", dtype=torch.float32)
-    _need(k_new, "k_new")
-    _need(v_new, "v_new", dtype=k_new.dtype)
-    _need(block_table, "block_table", dtype=torch.int32)
-    _need(seq_lens, "seq_lens", dtype=torch.int32)
+    _dims(k_cache, "k_cache", (None,) * 4)
     nb, bs, h_kv, d = k_cache.shape
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(v_scale.shape) != (nb, bs, h_kv):
-        raise KvdError("v_cache must match k_cache and v_scale be [num_blocks, 16, H_kv]")
-    if tuple(k_scale.shape) != (h_kv, d):
-        raise KvdError("k_scale must be [H_kv, d]")
+    _dims(v_cache, "v_cache", tuple(k_cache.shape))
+    _dims(v_scale, "v_scale", (nb, bs, h_kv))
+    _dims(k_scale, "k_scale", (h_kv, d))
+    _dims(k_new, "k_new", (None, h_kv, d))
     B = k_new.shape[0]
-    if tuple(k_new.shape) != (B, h_kv, d) or tuple(v_new.shape) != (B, h_kv, d):
-        raise KvdError("k_new and v_new must be [B, H_kv, d]")
+    _dims(v_new, "v_new", (B, h_kv, d))
+    _batch(seq_lens, block_table, B)
+    _need(k_cache, "k_cache", dtype=code_dtype)
+    _need(v_cache, "v_cache", dtype=code_dtype, like=k_cache)
+    _need(v_scale, "v_scale", dtype=torch.float32, like=k_cache)
+    _need(k_scale, "k_scale", dtype=torch.float32, like=k_cache)
+    _need(k_new, "k_new", like=k_cache)
+    _need(v_new, "v_new", dtype=k_new.dtype, like=k_cache)
+    _need(block_table, "block_table", dtype=torch.int32, like=k_cache)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, like=k_cache)
     status = getattr(lib, name)(_ptr(k_cache), _ptr(v_cache), _ptr(v_scale), _ptr(k_new),
                                 _ptr(v_new), _ptr(k_scale), _ptr(block_table), _ptr(seq_lens), B,
                                 h_kv, d, bs, block_table.shape[1], nb, _dtype_code(k_new),
@@ -476,23 +528,26 @@ def _append_bytes(name, code_dtype, k_cache, v_cache, v_scale, k_new, v_new, k_s
 
 
 def _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len, scale,
-               partition_tokens, ws, code_dtype=torch.int8):
-    for t, n in ((q, "q"), (block_table, "block_table"), (seq_lens, "seq_lens"),
-                 (ws, "workspace")):
-        _need(t, n)
-    _need(q, "q", dtype=torch.bfloat16)
-    _need(k_cache, "k_cache", dtype=code_dtype)
-    _need(v_cache, "v_cache", dtype=code_dtype)
-    _need(k_scale, "k_scale", dtype=torch.float32)
-    _need(v_scale, "v_scale", dtype=torch.float32)
-    _need(block_table, "block_table", dtype=torch.int32)
-    _need(seq_lens, "seq_lens", dtype=torch.int32)
+               partition_tokens, ws, code_dtype=torch.int8, out=None):
+    _dims(q, "q", (None,) * 3)
     B, h_q, d = q.shape
-    nb, bs, h_kv, d2 = k_cache.shape
-    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise KvdError("q, k_cache and v_cache head sizes disagree")
-    if tuple(k_scale.shape) != (h_kv, d) or tuple(v_scale.shape) != (nb, bs, h_kv):
-        raise KvdError("k_scale must be [H_kv, d] and v_scale [num_blocks, 16, H_kv]")
+    _dims(k_cache, "k_cache", (None, None, None, d))
+    _dims(v_cache, "v_cache", tuple(k_cache.shape))
+    nb, bs, h_kv, _ = k_cache.shape
+    _dims(k_scale, "k_scale", (h_kv, d))
+    _dims(v_scale, "v_scale", (nb, bs, h_kv))
+    _batch(seq_lens, block_table, B)
+    if out is not None:
+        _dims(out, "out", (B, h_q, d))
+        _need(out, "out", dtype=torch.bfloat16, like=q)
+    _need(q, "q", dtype=torch.bfloat16)
+    _need(ws, "workspace", like=q)
+    _need(k_cache, "k_cache", dtype=code_dtype, like=q)
+    _need(v_cache, "v_cache", dtype=code_dtype, like=q)
+    _need(k_scale, "k_scale", dtype=torch.float32, like=q)
+    _need(v_scale, "v_scale", dtype=torch.float32, like=q)
+    _need(block_table, "block_table", dtype=torch.int32, like=q)
+    _need(seq_lens, "seq_lens", dtype=torch.int32, like=q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
@@ -506,6 +561,8 @@ def decode_attn_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, s
                            stream=None):
     """Decode attention of bf16 q [B, H_q, d] over an INT8 paged cache; returns
     the bf16 output."""
+    _dims(q, "q", (None,) * 3)
+    _dims(k_cache, "k_cache", (None,) * 4)
     B, h_q, d = q.shape
     h_kv = k_cache.shape[2]
     if workspace is None:
@@ -513,9 +570,8 @@ def decode_attn_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, s
                                     device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=torch.bfloat16)
     args = _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len,
-                      scale, partition_tokens, workspace)
+                      scale, partition_tokens, workspace, out=out)
     _check(lib.decode_attn_paged_int8(_ptr(out), *args, _stream(stream)),
            "decode_attn_paged_int8")
     return out
@@ -536,6 +592,8 @@ def decode_attn_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, se
                           stream=None):
     """Decode attention of bf16 q [B, H_q, d] over an FP8 (E4M3, uint8 codes)
     paged cache; returns the bf16 output."""
+    _dims(q, "q", (None,) * 3)
+    _dims(k_cache, "k_cache", (None,) * 4)
     B, h_q, d = q.shape
     h_kv = k_cache.shape[2]
     if workspace is None:
@@ -543,9 +601,8 @@ def decode_attn_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, se
                                     device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=torch.bfloat16)
     args = _int8_args(q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, max_seq_len,
-                      scale, partition_tokens, workspace, code_dtype=torch.uint8)
+                      scale, partition_tokens, workspace, code_dtype=torch.uint8, out=out)
     _check(lib.decode_attn_paged_fp8(_ptr(out), *args, _stream(stream)), "decode_attn_paged_fp8")
     return out
 
@@ -593,8 +650,10 @@ def validate_finite(values, dtype="bf16"):
 def kv_copy_blocks(cache, pairs, stream=None):
     """Copy whole blocks of ``cache`` [num_blocks, ...]: block pairs[i, 0] onto
     block pairs[i, 1] (device int32 [n, 2])."""
+    if pairs is None or pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
+        raise KvdError("pairs must be [n, 2]")
     _need(cache, "cache")
-    _need(pairs, "pairs", dtype=torch.int32)
+    _need(pairs, "pairs", dtype=torch.int32, like=cache)
     n = pairs.shape[0] if pairs.numel() else 0
     nb = cache.shape[0]
     block_bytes = cache[0].numel() * cache.element_size()
@@ -699,12 +758,19 @@ def kv_append_paged_multi(k_cache, v_cache, k_new, v_new, cu_rows, block_table, 
                           max_rows, stream=None):
     """Write n_b = cu_rows[b+1] - cu_rows[b] new rows of each sequence into
     positions [seq_lens[b] - n_b, seq_lens[b]); k_new/v_new: [N, H_kv, d]."""
-    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new")):
-        _need(t, n, dtype=k_cache.dtype)
-    for t, n in ((cu_rows, "cu_rows"), (block_table, "block_table"), (seq_lens, "seq_lens")):
-        _need(t, n, dtype=torch.int32)
+    _dims(k_cache, "k_cache", (None,) * 4)
     nb, bs, h_kv, d = k_cache.shape
+    _dims(v_cache, "v_cache", tuple(k_cache.shape))
+    _dims(k_new, "k_new", (None, h_kv, d))
+    _dims(v_new, "v_new", tuple(k_new.shape))
+    _dims(seq_lens, "seq_lens", (None,))
     B = seq_lens.shape[0]
+    _batch(seq_lens, block_table, B)
+    _dims(cu_rows, "cu_rows", (B + 1,))
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, dtype=k_cache.dtype, like=k_cache)
+    for t, n in ((cu_rows, "cu_rows"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need(t, n, dtype=torch.int32, like=k_cache)
     status = lib.kv_append_paged_multi(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                                        _ptr(cu_rows), _ptr(block_table), _ptr(seq_lens), B,
                                        int(max_rows), h_kv, d, bs, block_table.shape[1], nb,
@@ -716,20 +782,24 @@ def prefill_attn_paged(q, k_cache, v_cache, cu_rows, block_table, seq_lens, max_
                        max_rows, scale=None, out=None, stream=None):
     """Causal attention of the new rows q [N, H_q, d] (bf16) over the paged
     cache, which already holds them; returns out [N, H_q, d]."""
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need(t, n, dtype=torch.bfloat16)
-    for t, n in ((cu_rows, "cu_rows"), (block_table, "block_table"), (seq_lens, "seq_lens")):
-        _need(t, n, dtype=torch.int32)
+    _dims(q, "q", (None,) * 3)
     N, h_q, d = q.shape
-    nb, bs, h_kv, d2 = k_cache.shape
-    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise KvdError("q, k_cache and v_cache head sizes disagree")
+    _dims(k_cache, "k_cache", (None, None, None, d))
+    _dims(v_cache, "v_cache", tuple(k_cache.shape))
+    nb, bs, h_kv, _ = k_cache.shape
+    _dims(seq_lens, "seq_lens", (None,))
+    B = seq_lens.shape[0]
+    _batch(seq_lens, block_table, B)
+    _dims(cu_rows, "cu_rows", (B + 1,))
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", dtype=torch.bfloat16)
+    _dims(out, "out", (N, h_q, d))
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (out, "out")):
+        _need(t, n, dtype=torch.bfloat16, like=q)
+    for t, n in ((cu_rows, "cu_rows"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need(t, n, dtype=torch.int32, like=q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    B = seq_lens.shape[0]
     status = lib.prefill_attn_paged(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(cu_rows), _ptr(block_table), _ptr(seq_lens), B,
                                     int(max_rows), h_q, h_kv, d, bs, block_table.shape[1], nb,

@@ -114,6 +114,10 @@ DECODE_CASES = [
     ("r2-d64", dict(B=3, H_q=8, H_kv=4, d=64, lens=[33, 999, 1], pt=0)),
     ("r8-d128", dict(B=2, H_q=64, H_kv=8, d=128, lens=[2500, 300], pt=0)),
     ("mqa-d32", dict(B=2, H_q=4, H_kv=1, d=32, lens=[129, 640], pt=64)),
+    # history codes over every finite magnitude 0x00 .. 0x7E (values up to 448
+    # times the scale), both signs
+    ("gqa-r4-full-range", dict(B=4, H_q=32, H_kv=8, d=128, lens=[17, 700, 2049, 4000], pt=0,
+                               full_range=True)),
 ]
 
 
@@ -121,7 +125,11 @@ DECODE_CASES = [
 def test_decode_fp8_parity(name, c):
     log(f"fp8 decode {name}")
     inp = make_paged_decode_fp8(np.random.default_rng(zlib.crc32(name.encode()) + 11), c["B"],
-                                c["H_q"], c["H_kv"], c["d"], c["lens"])
+                                c["H_q"], c["H_kv"], c["d"], c["lens"],
+                                full_range=c.get("full_range", False))
+    if c.get("full_range"):
+        hist = inp.kq_pool[np.isin(np.arange(inp.num_blocks), inp.block_table)] & 0x7F
+        assert set(np.unique(hist).tolist()) >= set(range(0x7F))  # 0x7F: the NaN sentinel
     dev = Fp8Dev(inp)
     dev.append()
     out = kvd.decode_attn_paged_fp8(dev.q, dev.kq, dev.vq, dev.ks, dev.vs, dev.table, dev.seq,

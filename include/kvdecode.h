@@ -289,6 +289,37 @@ int decode_attn_paged_append_partials(const void* q, void* k_cache, void* v_cach
                                       void* stream);
 
 /*
+ * decode_attn_paged_append_noalloc -- decode_attn_paged_append for callers
+ * that cannot allocate device memory: code recorded under HIP graph capture,
+ * tight serving loops, and harnesses that forbid hipMalloc.  It takes no
+ * workspace argument and calls no allocating routine: the partial results go
+ * to a fixed device scratch array of KVD_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * GPU, which the library holds from its first use on that GPU until the
+ * process ends.
+ *   Arguments, preconditions and results as for decode_attn_paged_append
+ *   (the caller passes every input and `out`).
+ *   Returns KVD_ERR_WORKSPACE when the call needs more than
+ *   KVD_NOALLOC_SCRATCH_BYTES (decode_attn_workspace_bytes of the same sizes),
+ *   KVD_ERR_HIP when the scratch address cannot be looked up.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents (nothing in it needs clearing: every value the merge
+ *   reads is written by the same call first).  Calls that can overlap on one
+ *   GPU -- on different streams, or from different host threads -- race on
+ *   it; serialise them.
+ */
+#define KVD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int decode_attn_paged_append_noalloc(void* out, const void* q, void* k_cache, void* v_cache,
+                                     const void* k_new, const void* v_new,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int max_blocks_per_seq, int num_blocks,
+                                     int max_seq_len, float scale, int partition_tokens,
+                                     kvd_dtype_t dtype, void* stream);
+
+/* Size in bytes of the scratch array of decode_attn_paged_append_noalloc. */
+size_t decode_attn_noalloc_scratch_bytes(void);
+
+/*
  * decode_attn_mla -- absorbed multi-head latent attention decode (bf16).
  *
  * The cache keeps one row per token: the latent c_t (d_c values) followed by

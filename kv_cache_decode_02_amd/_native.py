@@ -51,6 +51,11 @@ lib.decode_attn_paged_append.restype = _i
 lib.decode_attn_paged_append.argtypes = [_vp] + _APPEND_ARGS
 lib.decode_attn_paged_append_partials.restype = _i
 lib.decode_attn_paged_append_partials.argtypes = _APPEND_ARGS
+lib.decode_attn_paged_append_noalloc.restype = _i
+# the append arguments without the workspace pointer and byte count
+lib.decode_attn_paged_append_noalloc.argtypes = [_vp] + _APPEND_ARGS[:-4] + [_i, _vp]
+lib.decode_attn_noalloc_scratch_bytes.restype = _sz
+lib.decode_attn_noalloc_scratch_bytes.argtypes = []
 _MLA_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 lib.decode_attn_mla.restype = _i
 lib.decode_attn_mla.argtypes = [_vp] + _MLA_ARGS
@@ -250,7 +255,9 @@ def _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
     if out is not None:
         _dims(out, "out", (B, h_q, d))
         _need(out, "out", dtype=q.dtype, like=q)
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (ws, "workspace")):
+    # ws None: the allocation-free entry point, which takes no workspace
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")) + (
+            () if ws is None else ((ws, "workspace"),)):
         _need(t, n, like=q)
     _need(block_table, "block_table", dtype=torch.int32, like=q)
     _need(seq_lens, "seq_lens", dtype=torch.int32, like=q)
@@ -260,7 +267,8 @@ def _paged_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
         scale = 1.0 / math.sqrt(d)
     return [_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
             B, h_q, h_kv, d, bs, block_table.shape[1], nb, int(max_seq_len), float(scale),
-            int(partition_tokens), _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q)]
+            int(partition_tokens), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+            _dtype_code(q)]
 
 
 def decode_attn_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=None,
@@ -364,6 +372,28 @@ def decode_attn_paged_append_partials(q, k_cache, v_cache, k_new, v_new, block_t
                         scale, partition_tokens, workspace)
     _check(lib.decode_attn_paged_append_partials(*args, _stream(stream)),
            "decode_attn_paged_append_partials")
+
+
+def decode_attn_paged_append_noalloc(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens,
+                                     max_seq_len, out, scale=None, partition_tokens=0,
+                                     stream=None):
+    """decode_attn_paged_append without a workspace argument and without any
+    device allocation: the library's per-GPU scratch array holds the partial
+    results (at most decode_attn_noalloc_scratch_bytes()).  ``out`` is
+    required; calls that overlap on one GPU race on the scratch array."""
+    if out is None:
+        raise KvdError("out is required (the allocation-free call allocates nothing)")
+    args = _append_args(q, k_cache, v_cache, k_new, v_new, block_table, seq_lens, max_seq_len,
+                        scale, partition_tokens, None, out)
+    # the C entry point takes no workspace: drop the pointer and byte count
+    del args[-3:-1]
+    _check(lib.decode_attn_paged_append_noalloc(_ptr(out), *args, _stream(stream)),
+           "decode_attn_paged_append_noalloc")
+    return out
+
+
+def decode_attn_noalloc_scratch_bytes():
+    return int(lib.decode_attn_noalloc_scratch_bytes())
 
 
 def decode_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_tokens=0,

@@ -484,6 +484,43 @@ int decode_attn_paged_append(void* out, const void* q, void* k_cache, void* v_ca
                            partition_tokens, workspace, workspace_bytes, dtype, stream);
 }
 
+int decode_attn_paged_append_noalloc(void* out, const void* q, void* k_cache, void* v_cache,
+                                     const void* k_new, const void* v_new,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int max_blocks_per_seq, int num_blocks,
+                                     int max_seq_len, float scale, int partition_tokens,
+                                     kvd_dtype_t dtype, void* stream) {
+  // The scratch array serves as the workspace; everything else is the
+  // checked path of decode_attn_paged_append.  No allocation happens here:
+  // the array was placed in device memory when the library was loaded on
+  // this device.
+  if (batch == 0)
+    return decode_attn_paged_append(out, q, k_cache, v_cache, k_new, v_new, block_table,
+                                    seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                    block_size, max_blocks_per_seq, num_blocks, max_seq_len,
+                                    scale, partition_tokens, nullptr, 0, dtype, stream);
+  const size_t need = decode_attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                  max_seq_len, partition_tokens);
+  if (need == 0) {
+    // Sizes the planner rejects: let the shared checks name the error.
+    return decode_attn_paged_append(out, q, k_cache, v_cache, k_new, v_new, block_table,
+                                    seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                    block_size, max_blocks_per_seq, num_blocks, max_seq_len,
+                                    scale, partition_tokens, nullptr, 0, dtype, stream);
+  }
+  if (need > kNoAllocScratchBytes) return KVD_ERR_WORKSPACE;
+  hipError_t e = hipSuccess;
+  void* ws = noalloc_scratch(&e);
+  if (!ws) return KVD_ERR_HIP;
+  return decode_attn_paged_append(out, q, k_cache, v_cache, k_new, v_new, block_table, seq_lens,
+                                  batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_blocks_per_seq, num_blocks, max_seq_len, scale,
+                                  partition_tokens, ws, kNoAllocScratchBytes, dtype, stream);
+}
+
+size_t decode_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
 static int append_bytes(void* k_cache, void* v_cache, float* v_scale, const void* k_new,
                         const void* v_new, const float* k_scale, const int32_t* block_table,
                         const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,

@@ -142,6 +142,13 @@ struct MlaLaunch {
   const void* c_new;
 };
 
+// Allocation-free entry point: size of the per-device scratch array that
+// stands in for the caller's workspace (64 MiB), and its device address on
+// the current device (looked up once per device; NULL and *err set on a HIP
+// error).
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(64) << 20;
+void* noalloc_scratch(hipError_t* err);
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream);
 hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream);

@@ -217,3 +217,15 @@ def test_copy_blocks():
     _reaches_device_check(kvd.kv_copy_blocks, cache, torch.zeros(2, 2, dtype=i32))
     _refused(kvd.kv_copy_blocks, "pairs", cache, torch.zeros(2, 3, dtype=i32))
     _refused(kvd.kv_copy_blocks, "pairs", cache, torch.zeros(4, dtype=i32))
+
+
+def test_noalloc_entry_point():
+    fn = kvd.decode_attn_paged_append_noalloc
+    out = torch.zeros(B, HQ, D, dtype=bf)
+    _reaches_device_check(fn, **paged(), **new_rows(), out=out)
+    _refused(fn, "out", **paged(), **new_rows(), out=None)
+    _refused(fn, "out", **paged(), **new_rows(), out=torch.zeros(B, HQ, D + 1, dtype=bf))
+    for name, over in BAD_BATCH:
+        _refused(fn, name, **paged(**over), **new_rows(), out=out)
+    _refused(fn, "k_new", **paged(), **new_rows(k_new=torch.zeros(B + 1, HKV, D, dtype=bf)),
+             out=out)

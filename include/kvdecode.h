@@ -320,6 +320,23 @@ int decode_attn_paged_append_noalloc(void* out, const void* q, void* k_cache, vo
 size_t decode_attn_noalloc_scratch_bytes(void);
 
 /*
+ * kvd_stream_read -- measurement aid, not a step of the decode: reads
+ * `bytes` of device memory once (16-byte loads, each of 2048 workgroups of
+ * 256 threads streaming one contiguous span) and writes almost nothing, so that its
+ * duration gives the device's sustained HBM read rate, the practical ceiling
+ * of a step that is bound by reading the cache ("KV-Cache——为什么AI回复越来
+ * 越快", 04: decode is limited by moving the cache, not by arithmetic).
+ *   src   device memory, 16-byte aligned; bytes a multiple of 16
+ *   sink  device memory of at least kvd_stream_read_sink_bytes() bytes;
+ *         a word of it is written only if a thread's fold of its words
+ *         equals a fixed sentinel (contents otherwise untouched)
+ * Returns KVD_OK, KVD_ERR_NULL, KVD_ERR_SHAPE (alignment / size),
+ * KVD_ERR_WORKSPACE (sink too small) or KVD_ERR_HIP.  Asynchronous on stream.
+ */
+size_t kvd_stream_read_sink_bytes(void);
+int kvd_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+
+/*
  * decode_attn_mla -- absorbed multi-head latent attention decode (bf16).
  *
  * The cache keeps one row per token: the latent c_t (d_c values) followed by

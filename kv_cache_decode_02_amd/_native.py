@@ -56,6 +56,10 @@ lib.decode_attn_paged_append_noalloc.restype = _i
 lib.decode_attn_paged_append_noalloc.argtypes = [_vp] + _APPEND_ARGS[:-4] + [_i, _vp]
 lib.decode_attn_noalloc_scratch_bytes.restype = _sz
 lib.decode_attn_noalloc_scratch_bytes.argtypes = []
+lib.kvd_stream_read_sink_bytes.restype = _sz
+lib.kvd_stream_read_sink_bytes.argtypes = []
+lib.kvd_stream_read.restype = _i
+lib.kvd_stream_read.argtypes = [_vp, _sz, _vp, _sz, _vp]
 _MLA_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 lib.decode_attn_mla.restype = _i
 lib.decode_attn_mla.argtypes = [_vp] + _MLA_ARGS
@@ -394,6 +398,21 @@ def decode_attn_paged_append_noalloc(q, k_cache, v_cache, k_new, v_new, block_ta
 
 def decode_attn_noalloc_scratch_bytes():
     return int(lib.decode_attn_noalloc_scratch_bytes())
+
+
+def stream_read(src, sink, stream=None):
+    """Measurement aid: one streaming read of the device tensor ``src`` (its
+    byte size a multiple of 16); ``sink`` a device tensor of at least
+    stream_read_sink_bytes() bytes."""
+    _need(src, "src")
+    _need(sink, "sink", like=src)
+    _check(lib.kvd_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                               sink.numel() * sink.element_size(), _stream(stream)),
+           "kvd_stream_read")
+
+
+def stream_read_sink_bytes():
+    return int(lib.kvd_stream_read_sink_bytes())
 
 
 def decode_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_tokens=0,

@@ -521,6 +521,19 @@ int decode_attn_paged_append_noalloc(void* out, const void* q, void* k_cache, vo
 
 size_t decode_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
+size_t kvd_stream_read_sink_bytes(void) {
+  return static_cast<size_t>(stream_read_groups()) * 256 * sizeof(uint32_t);
+}
+
+int kvd_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+  if (bytes == 0) return KVD_OK;
+  if (!src || !sink) return KVD_ERR_NULL;
+  if (bytes % 16 != 0 || !aligned16(src)) return KVD_ERR_SHAPE;
+  if (sink_bytes < kvd_stream_read_sink_bytes()) return KVD_ERR_WORKSPACE;
+  return hip_status(launch_stream_read(src, bytes, static_cast<uint32_t*>(sink),
+                                       static_cast<hipStream_t>(stream)));
+}
+
 static int append_bytes(void* k_cache, void* v_cache, float* v_scale, const void* k_new,
                         const void* v_new, const float* k_scale, const int32_t* block_table,
                         const int32_t* seq_lens, int batch, int num_kv_heads, int head_dim,

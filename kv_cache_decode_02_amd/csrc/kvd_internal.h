@@ -149,6 +149,11 @@ struct MlaLaunch {
 constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(64) << 20;
 void* noalloc_scratch(hipError_t* err);
 
+// Streaming-read probe: workgroups launched (the sink holds one word per
+// thread of them), and the launch over `bytes` (a multiple of 16).
+int stream_read_groups();
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_append(const AppendLaunch& a, hipStream_t stream);
 hipError_t launch_append_int8(const AppendInt8Launch& a, hipStream_t stream);

@@ -69,34 +69,8 @@ static_assert(kKSteps % kKBatch == 0, "batched K-steps");
 // Each 16-token block (18432 bytes) is fetched by 256 threads: 4 x 16 B + 8 B.
 static_assert(kBlockTokens * kRowBytes == 256 * (4 * 16 + 8), "tile load split");
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  uint4 u = make_uint4(a, b, c, d);
-  return __builtin_bit_cast(bf16x8_t, u);
-}
-
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Combine a value over the four 16-lane rows of the wave (lanes l, l ^ 16,
-// l ^ 32, l ^ 48).  Each swap returns the lane's own value and the value of
-// its partner row, so the combination is the same in every lane.
-__device__ __forceinline__ float row_max4(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float row_sum4(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 struct MlaLaunchDev {

@@ -30,6 +30,9 @@
 //     unit), paged_partials_kernel;
 //   balanced split (automatic mode): one workgroup per compute unit, each
 //     streaming an equal share of all blocks, paged_balanced_kernel.
+#include <stdlib.h>
+#include <string.h>
+
 #include "kvd_device.h"
 #include "kvd_internal.h"
 
@@ -44,18 +47,22 @@ constexpr float kRaise = 8.0f;
 constexpr int kMaxPartitionBlocks = 64;  // one block id per lane
 constexpr int kMinPieceBlocks = kBalancedMinPieceBlocks;
 // Relative share of a workgroup on an even and an odd XCD (workgroup k runs
-// on XCD k mod 8).  Measured on MI355X with the GQA decode batch: streaming
-// the same number of blocks takes the odd XCDs 6-9% longer, on every
-// repetition and on different boards; a sweep of the even share over 1.00 ..
-// 1.17 gives the shortest kernel at 1.11 - 1.14.
-constexpr long long kEvenXcdShare = 1120;
+// on XCD k mod 8), per 1000 for an odd one; each worker flavour sets its
+// even share (kEvenXcdShare).  Measured on MI355X with the GQA decode batch:
+// with the VALU flavour, streaming the same number of blocks takes the odd
+// XCDs 6-9% longer and a sweep of the even share over 1.00 .. 1.17 gives the
+// shortest kernel at 1.11 - 1.14; the MFMA flavour does best near 1.06
+// (per-workgroup end times show which XCDs lag changing from run to run).
 constexpr long long kOddXcdShare = 1000;
 // Virtual blocks charged for each segment (sequence, unit group) a share
 // starts: the restart (query and block-id loads, then the first blocks'
 // loads) costs a few blocks' time.  Measured on MI355X with the GQA decode
 // batch over 0 .. 6: shortest at 3 - 4 (1.3% below 1), the MHA batch
 // unchanged.
-constexpr int kSegmentCost = 4;
+#ifndef KVD_SEGMENT_COST
+#define KVD_SEGMENT_COST 4
+#endif
+constexpr int kSegmentCost = KVD_SEGMENT_COST;
 
 template <int KT, int D>
 struct RowShape {
@@ -559,6 +566,298 @@ __device__ __forceinline__ int seq_blocks(const PagedLaunch& a, int b) {
   return (len + kBlockTokens - 1) / kBlockTokens - first_visible(a, len) / kBlockTokens;
 }
 
+// ---- Workers: one unit of work (sequence, K/V head, chunk of query heads)
+// streamed over a range of blocks and written as one piece ---------------------
+
+// VALU flavour: lane groups of 8, dot2 scores, fp32 FMA values (above).
+template <int KT, int D, int HPW, int NBUF>
+struct ValuWorker {
+  static constexpr int kLdsPerWave = 0;
+  static constexpr long long kEvenXcdShare = 1120;
+  static __device__ __forceinline__ int heads_per_wave(int /*ratio*/) { return HPW; }
+  static __device__ __forceinline__ void unit(const PagedLaunch& a, int lane, unsigned char* /*lds*/,
+                                              int b, int g, int h0, int j_begin, int j_end,
+                                              int t_start, int t_end, bool fused, bool write_new,
+                                              size_t slot0, size_t P) {
+    HeadState<HPW, D / 8> st;
+    attend<KT, D, HPW, NBUF>(a, lane, b, g, h0, j_begin, j_end, t_start, t_end, st, fused,
+                             write_new);
+    write_partial<KT, D, HPW>(a, lane, slot0, P, pick_group(st, lane));
+  }
+  static __device__ __forceinline__ void empty(const PagedLaunch& a, int lane, size_t slot0,
+                                               size_t P) {
+    HeadState<HPW, D / 8> st;
+    reset_state(st);
+    write_partial<KT, D, HPW>(a, lane, slot0, P, pick_group(st, lane));
+  }
+};
+
+// MFMA flavour (bf16 caches, groups of up to 16 query heads per wave).  For
+// one 16-token block of K/V head g and the wave's query heads:
+//   scores  S^T[token][head] = K_blk[16 x D] . Q^T[D x 16]: D/32 MFMA
+//           16x16x32; K rows go straight from HBM into the A operand (lane
+//           (G, i) = (lane / 16, lane % 16) holds token i, dimensions
+//           32 s + 8 G .. + 7 of K-step s), the queries stay in registers as
+//           the B operand (head i, same dimensions; heads past the group are
+//           zero), and lane (G, i) ends with head i, tokens 4 G .. 4 G + 3.
+//   softmax online per head with a lazily raised reference max, which is
+//           uniform over the four lanes of a head (row_max4), so that every
+//           weight of a head meets the same reference in the product below.
+//   values  O^T[D x 16] += V_blk^T[D x 16] . P^T[16 x 16]: D/16 column tiles,
+//           MFMA 16x16x16 with each weight as a bf16 value plus its bf16
+//           remainder (two MFMAs, about 16 bits of weight; the running sum
+//           takes the fp32 weights).  The weights are the B operand exactly
+//           as the score MFMA left them (head i, tokens 4 G .. + 3); the V
+//           operand (one dimension per lane, four tokens along K) is V_blk
+//           transposed: the wave writes its block of V into its own LDS
+//           slice (token rows, 16-byte chunks XOR-swizzled by row so that
+//           the writes and the transpose reads are free of bank conflicts)
+//           and reads it back with ds_read_b64_tr_b16.  Lane (G, i) ends
+//           with head i and dimensions 16 t + 4 G .. + 3 of tile t, so a
+//           rescale of head i touches only its own lane's registers.
+// Per block and wave this is D/32 + D/8 MFMAs and ~50 VALU instructions
+// for all heads of the group, against ~300 VALU instructions per 4 heads in
+// the VALU flavour.
+template <int D>
+struct MShape {
+  static constexpr int KS = D / 32;   // K-steps of the scores
+  static constexpr int NT = D / 16;   // 16-dimension column tiles of the output
+  static constexpr int C = D / 8;     // 16-byte chunks per row of one K/V head
+  static constexpr int ROWB = 2 * D;  // bytes per row of one K/V head
+  // Chunk position of chunk c of LDS row r (XOR swizzle).
+  static __device__ __forceinline__ int pos(int r, int c) { return c ^ ((r * D / 128) % C); }
+};
+
+template <int D>
+struct MFrag {
+  uint32_t k[MShape<D>::KS][4];
+  uint32_t v[MShape<D>::KS][4];
+};
+
+// Rows of K/V head g for the lane: token i of the block, dimensions
+// 32 s + 8 G .. + 7 for each K-step s; rows at or past nvalid read as zeros.
+template <int D>
+__device__ __forceinline__ void mfma_rows(MFrag<D>& f, const uint32_t* kbase, const uint32_t* vbase,
+                                          const PagedLaunch& a, int lane, int g, int nvalid) {
+  const int tok_bytes = a.num_kv_heads * MShape<D>::ROWB;
+  const int bytes = nvalid * tok_bytes;
+  const BufRsrc rk = make_rsrc(kbase, bytes);
+  const BufRsrc rv = make_rsrc(vbase, bytes);
+  const uint32_t off = static_cast<uint32_t>((lane & 15) * tok_bytes + g * MShape<D>::ROWB +
+                                             16 * (lane >> 4));
+#pragma unroll
+  for (int s = 0; s < MShape<D>::KS; ++s) {
+    buffer_load_words<4>(f.k[s], rk, off + 64 * s);
+    buffer_load_words<4>(f.v[s], rv, off + 64 * s);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void mfma_block_rows(MFrag<D>& f, const PagedLaunch& a, int lane, int g,
+                                                int blk, int nvalid) {
+  const size_t words = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens *
+                       a.num_kv_heads * (D / 2);
+  mfma_rows<D>(f, static_cast<const uint32_t*>(a.k_cache) + words,
+               static_cast<const uint32_t*>(a.v_cache) + words, a, lane, g, nvalid);
+}
+
+template <int D>
+struct MState {
+  f32x4_t acc[MShape<D>::NT];  // O^T: head lane % 16, dims 16 t + 4 (lane / 16) + j
+  float m;                     // reference max of the lane's head (log2 units)
+  float l;                     // the lane's share of the weight sum
+};
+
+// One block through the online softmax: tokens [nskip, nvalid) count.  `lds`
+// is the wave's LDS slice (16 rows of one K/V head).
+template <int D>
+__device__ __forceinline__ void mfma_block(const MFrag<D>& f, const uint32_t (&q)[MShape<D>::KS][4],
+                                           unsigned char* lds, int lane, int nskip, int nvalid,
+                                           float sl2, MState<D>& st) {
+  using S = MShape<D>;
+  const int G = lane >> 4, i = lane & 15;
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        as_bf16x8(f.k[s][0], f.k[s][1], f.k[s][2], f.k[s][3]),
+        as_bf16x8(q[s][0], q[s][1], q[s][2], q[s][3]), sc, 0, 0, 0);
+  // V rows into the LDS slice: row i, chunk 4 s + G.
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s)
+    *reinterpret_cast<uint4*>(lds + i * S::ROWB + S::pos(i, 4 * s + G) * 16) =
+        make_uint4(f.v[s][0], f.v[s][1], f.v[s][2], f.v[s][3]);
+  float z[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 4 * G + j;
+    z[j] = (t >= nskip && t < nvalid) ? sc[j] * sl2 : -INFINITY;
+    mx = fmaxf(mx, z[j]);
+  }
+  mx = row_max4(mx);
+  const bool up = mx > st.m + kRaise;
+  if (__builtin_amdgcn_ballot_w64(up)) {
+    const float mn = up ? mx : st.m;
+    const float alpha = exp2_fast(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < S::NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.acc[t][j] *= alpha;
+    st.m = mn;
+  }
+  float p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = exp2_fast(z[j] - st.m);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  const uint32_t h0 = pack_bf16x2(p[0], p[1]), h1 = pack_bf16x2(p[2], p[3]);
+  const uint32_t r0 = pack_bf16x2(p[0] - bf16_lo(h0), p[1] - bf16_hi(h0));
+  const uint32_t r1 = pack_bf16x2(p[2] - bf16_lo(h1), p[3] - bf16_hi(h1));
+  const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h0, h1));
+  const s16x4_t pr = __builtin_bit_cast(s16x4_t, make_uint2(r0, r1));
+  // Transpose reads: lane (G, i) addresses row 4 G + i / 4, dimensions
+  // 16 t + 4 (i % 4) .. + 3, and receives dimension 16 t + i of rows
+  // 4 G .. 4 G + 3.
+  const int rr = 4 * G + (i >> 2);
+  unsigned char* rbase = lds + rr * S::ROWB + 8 * (i & 1);
+#pragma unroll
+  for (int t = 0; t < S::NT; ++t) {
+    const int c = 2 * t + ((i & 3) >> 1);
+    const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(rbase + S::pos(rr, c) * 16));
+    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, st.acc[t], 0, 0, 0);
+    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pr, st.acc[t], 0, 0, 0);
+  }
+}
+
+template <int D, int NBUF>
+struct MfmaWorker {
+  using S = MShape<D>;
+  static constexpr int kLdsPerWave = 16 * S::ROWB;
+  static constexpr long long kEvenXcdShare = 1060;
+  static __device__ __forceinline__ int heads_per_wave(int ratio) { return ratio < 16 ? ratio : 16; }
+
+  static __device__ __forceinline__ void write(const PagedLaunch& a, int lane, size_t slot0,
+                                               size_t P, int nheads, const MState<D>& st) {
+    const int G = lane >> 4, i = lane & 15;
+    const float lsum = row_sum4(st.l);
+    if (i < nheads) {
+      const size_t slot = slot0 + i * P;
+      float* orow = a.ws_o + slot * D + 4 * G;
+#pragma unroll
+      for (int t = 0; t < S::NT; ++t)
+        *reinterpret_cast<float4*>(orow + 16 * t) =
+            make_float4(st.acc[t][0], st.acc[t][1], st.acc[t][2], st.acc[t][3]);
+      if (G == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * slot) = make_float2(st.m, lsum);
+    }
+  }
+
+  static __device__ __forceinline__ void empty(const PagedLaunch& a, int lane, size_t slot0,
+                                               size_t P) {
+    MState<D> st;
+#pragma unroll
+    for (int t = 0; t < S::NT; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = kMinusBig;
+    st.l = 0.f;
+    const int ratio = a.num_q_heads / a.num_kv_heads;
+    write(a, lane, slot0, P, heads_per_wave(ratio), st);
+  }
+
+  // Blocks [j_begin, j_end) of sequence b, K/V head g, query heads h0 ..;
+  // tokens before t_start or at or past t_end carry no weight.  With
+  // `fused` the range ends at position t_end - 1, which is taken from
+  // k_new / v_new as a one-token block after the others, and with
+  // `write_new` the wave also stores head g's part of those rows into their
+  // cache slot.
+  static __device__ __forceinline__ void unit(const PagedLaunch& a, int lane, unsigned char* lds,
+                                              int b, int g, int h0, int j_begin, int j_end,
+                                              int t_start, int t_end, bool fused, bool write_new,
+                                              size_t slot0, size_t P) {
+    const int ratio = a.num_q_heads / a.num_kv_heads;
+    const int nheads = heads_per_wave(ratio);
+    const int G = lane >> 4, i = lane & 15;
+    // Queries as the B operand: head h0 + i (zero past the wave's heads).
+    uint32_t q[S::KS][4];
+    {
+      const uint32_t* qrow = static_cast<const uint32_t*>(a.q) +
+                             (static_cast<size_t>(b) * a.num_q_heads + h0 + (i < nheads ? i : 0)) *
+                                 (D / 2);
+#pragma unroll
+      for (int s = 0; s < S::KS; ++s) {
+        load_words<4>(q[s], qrow + (32 * s + 8 * G) / 2);
+        if (i >= nheads) q[s][0] = q[s][1] = q[s][2] = q[s][3] = 0u;
+      }
+    }
+    MState<D> st;
+#pragma unroll
+    for (int t = 0; t < S::NT; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = kMinusBig;
+    st.l = 0.f;
+    const int t_last = t_end - 1;
+    if (fused) t_end = t_last;
+    const float sl2 = a.scale * kLog2e;
+    const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
+    MFrag<D> buf[NBUF];
+
+    for (int c0 = j_begin; c0 < j_end; c0 += kMaxPartitionBlocks) {
+      const int nblk = min(kMaxPartitionBlocks, j_end - c0);
+      const int my_id = lane < nblk ? trow[c0 + lane] : -1;
+      auto block_of = [&](int jj, int& nvalid) __attribute__((always_inline)) {
+        const int blk = __builtin_amdgcn_readlane(my_id, jj & (kWave - 1));
+        const bool ok = jj < nblk && blk >= 0 && blk < a.num_blocks;
+        nvalid = ok ? min(kBlockTokens, t_end - (c0 + jj) * kBlockTokens) : 0;
+        return blk;
+      };
+#pragma unroll
+      for (int s0 = 0; s0 < NBUF; ++s0) {
+        int nv;
+        const int blk = block_of(s0, nv);
+        mfma_block_rows<D>(buf[s0], a, lane, g, blk, nv);
+      }
+      for (int base = 0; base < nblk; base += NBUF) {
+#pragma unroll
+        for (int s0 = 0; s0 < NBUF; ++s0) {
+          const int jj = base + s0;
+          if (jj < nblk) {
+            int nv;
+            block_of(jj, nv);
+            mfma_block<D>(buf[s0], q, lds, lane, max(0, t_start - (c0 + jj) * kBlockTokens), nv,
+                          sl2, st);
+          }
+          int nv;
+          const int blk = block_of(jj + NBUF, nv);
+          mfma_block_rows<D>(buf[s0], a, lane, g, blk, nv);
+        }
+      }
+    }
+    if (fused) {
+      const int blk = wave_uniform(trow[t_last / kBlockTokens]);
+      if (blk >= 0 && blk < a.num_blocks) {
+        const size_t row_words = static_cast<size_t>(a.num_kv_heads) * (D / 2);
+        const size_t src = static_cast<size_t>(b) * row_words;
+        MFrag<D> f;
+        mfma_rows<D>(f, static_cast<const uint32_t*>(a.k_new) + src,
+                     static_cast<const uint32_t*>(a.v_new) + src, a, lane, g, 1);
+        mfma_block<D>(f, q, lds, lane, 0, 1, sl2, st);
+        if (write_new && i == 0) {
+          // Lanes (G, 0) hold dimensions 32 s + 8 G .. + 7 of the new rows.
+          const size_t dst = (static_cast<size_t>(blk) * kBlockTokens + t_last % kBlockTokens) *
+                                 row_words + g * (D / 2);
+          uint32_t* kd = static_cast<uint32_t*>(const_cast<void*>(a.k_cache)) + dst;
+          uint32_t* vd = static_cast<uint32_t*>(const_cast<void*>(a.v_cache)) + dst;
+#pragma unroll
+          for (int s = 0; s < S::KS; ++s) {
+            store_words<4>(kd + (32 * s + 8 * G) / 2, f.k[s]);
+            store_words<4>(vd + (32 * s + 8 * G) / 2, f.v[s]);
+          }
+        }
+      }
+    }
+    write(a, lane, slot0, P, nheads, st);
+  }
+};
+
 // NBUF: register buffers per wave (NBUF - 1 blocks in flight during compute).
 // WPE: waves per SIMD the register allocation is sized for.
 //
@@ -567,12 +866,15 @@ __device__ __forceinline__ int seq_blocks(const PagedLaunch& a, int b) {
 // KV heads (and head chunks) of one (sequence, partition), so a workgroup's
 // waves read the same blocks together: for 8 KV heads an 8-wave workgroup
 // reads whole contiguous token rows of every block.
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
+template <class W, int WPE, int WG>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_partials_kernel(PagedLaunch a) {
+  __shared__ __attribute__((aligned(16))) unsigned char wave_lds[WG * W::kLdsPerWave + 16];
   const int lane = threadIdx.x & (kWave - 1);
+  unsigned char* lds = wave_lds + wave_uniform(threadIdx.x >> 6) * W::kLdsPerWave;
   const int ratio = a.num_q_heads / a.num_kv_heads;
-  const int hchunks = ratio / HPW;
+  const int hpw = W::heads_per_wave(ratio);
+  const int hchunks = ratio / hpw;
 
   int u = wave_uniform(blockIdx.x * WG + (threadIdx.x >> 6));
   const int units = a.batch * a.num_partitions * a.num_kv_heads * hchunks;
@@ -590,24 +892,19 @@ void paged_partials_kernel(PagedLaunch a) {
   if (len <= p_begin) return;
   const int t_end = min(len, p_begin + a.partition_tokens);
   const int t_begin = max(p_begin, first_visible(a, len));
-  const int h0 = g * ratio + hc * HPW;
+  const int h0 = g * ratio + hc * hpw;
   const size_t P = a.num_partitions;
-  HeadState<HPW, D / 8> st;
+  const size_t slot0 = (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p;
   if (t_begin >= t_end) {
     // Before a sliding window: an empty piece (l = 0), which the merge skips.
-    reset_state(st);
-    write_partial<KT, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P,
-                              pick_group(st, lane));
+    W::empty(a, lane, slot0, P);
     return;
   }
   const int j0 = t_begin / kBlockTokens;
   const int nblk = (t_end + kBlockTokens - 1) / kBlockTokens - j0;
 
   const bool fused = a.k_new != nullptr && t_end == len;
-  attend<KT, D, HPW, NBUF>(a, lane, b, g, h0, j0, j0 + nblk, t_begin, t_end, st, fused,
-                                  hc == 0);
-  write_partial<KT, D, HPW>(a, lane, (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p, P,
-                              pick_group(st, lane));
+  W::unit(a, lane, lds, b, g, h0, j0, j0 + nblk, t_begin, t_end, fused, hc == 0, slot0, P);
 }
 
 // Balanced split (automatic mode).  The work list is every (sequence b,
@@ -626,17 +923,20 @@ void paged_partials_kernel(PagedLaunch a) {
 // segment's first item), and the workgroup of piece 0 records the number of
 // pieces for the merge.  Pieces of one (b, h) never exceed ceil(blocks /
 // kMinPieceBlocks) + 1.
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
+template <class W, int WPE, int WG>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_balanced_kernel(PagedLaunch a) {
+  __shared__ __attribute__((aligned(16))) unsigned char wave_lds[WG * W::kLdsPerWave + 16];
   // [batch + 1] blocks of the sequences before b, then [batch + 1] count of
   // the non-empty sequences before b.
   extern __shared__ int blk_prefix[];
   int* const seq_prefix = blk_prefix + a.batch + 1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x >> 6);
+  unsigned char* lds = wave_lds + wave * W::kLdsPerWave;
   const int ratio = a.num_q_heads / a.num_kv_heads;
-  const int hchunks = ratio / HPW;
+  const int hpw = W::heads_per_wave(ratio);
+  const int hchunks = ratio / hpw;
   const int units = a.num_kv_heads * hchunks;
   const int n_ug = (units + WG - 1) / WG;
 
@@ -685,7 +985,7 @@ void paged_balanced_kernel(PagedLaunch a) {
   const int per = max(kMinPieceBlocks, (vtotal + groups - 1) / groups);  // equal shares
   // Weight of the first k workgroups (even ones: indices 0, 2, 4, ...).
   auto weight = [&](int k) __attribute__((always_inline)) {
-    return kEvenXcdShare * ((k + 1) / 2) + kOddXcdShare * (k / 2);
+    return W::kEvenXcdShare * ((k + 1) / 2) + kOddXcdShare * (k / 2);
   };
   const long long wsum = weight(groups);
   auto bound = [&](int k) __attribute__((always_inline)) {
@@ -729,7 +1029,6 @@ void paged_balanced_kernel(PagedLaunch a) {
   if (item >= end) return;  // whole workgroup
 
   const size_t P = a.num_partitions;
-  HeadState<HPW, D / 8> st;
   while (item < end) {
     const int pb = prefix(b);
     const int nb = prefix(b + 1) - pb;
@@ -741,18 +1040,17 @@ void paged_balanced_kernel(PagedLaunch a) {
     const int u = ug * WG + wave;
     if (u < units) {
       const int g = u / hchunks, hc = u % hchunks;
-      const int h0 = g * ratio + hc * HPW;
+      const int h0 = g * ratio + hc * hpw;
       const int t_end = wave_uniform(min(a.seq_lens[b], a.max_seq_len));
       const int t_start = first_visible(a, t_end);
       const int js = t_start / kBlockTokens;  // the sequence's first visible block
       const bool fused = a.k_new != nullptr && seg_end == seg_begin + nb;
-      attend<KT, D, HPW, NBUF>(a, lane, b, g, h0, js + j0, js + j0 + (seg_end - item),
-                                      t_start, t_end, st, fused, hc == 0);
       const int first = owner(vpos(b, ug, nb, 0));
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
-      write_partial<KT, D, HPW>(a, lane, row0 * P + piece, P, pick_group(st, lane));
-      if (piece == 0 && lane < HPW)
+      W::unit(a, lane, lds, b, g, h0, js + j0, js + j0 + (seg_end - item), t_start, t_end, fused,
+              hc == 0, row0 * P + piece, P);
+      if (piece == 0 && lane < hpw)
         a.counts[row0 + lane] = owner(vpos(b, ug, nb, nb - 1)) - first + 1;
     }
     item = seg_end;
@@ -777,24 +1075,24 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
-hipError_t launch_variant(const PagedLaunch& a, hipStream_t stream) {
+template <class W, int WPE, int WG>
+hipError_t launch_variant(const PagedLaunch& a, int hpw, hipStream_t stream) {
   const int ratio = a.num_q_heads / a.num_kv_heads;
   const long long units = static_cast<long long>(a.batch) * a.num_partitions * a.num_kv_heads *
-                          (ratio / HPW);
+                          (ratio / hpw);
   const long long blocks = (units + WG - 1) / WG;
-  hipLaunchKernelGGL((paged_partials_kernel<KT, D, HPW, NBUF, WPE, WG>),
+  hipLaunchKernelGGL((paged_partials_kernel<W, WPE, WG>),
                      dim3(static_cast<unsigned>(blocks)), dim3(64 * WG), 0, stream, a);
   return hipGetLastError();
 }
 
 // Balanced split: as many workgroups as are resident at once (4 * WPE
 // wavefronts per compute unit, in workgroups of WG waves).
-template <int KT, int D, int HPW, int NBUF, int WPE, int WG>
+template <class W, int WPE, int WG>
 hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
   const size_t lds = 2 * static_cast<size_t>(a.batch + 1) * sizeof(int);
   const int groups = device_cus() * ((4 * WPE) / WG);
-  hipLaunchKernelGGL((paged_balanced_kernel<KT, D, HPW, NBUF, WPE, WG>),
+  hipLaunchKernelGGL((paged_balanced_kernel<W, WPE, WG>),
                      dim3(static_cast<unsigned>(groups)), dim3(64 * WG), lds, stream, a);
   return hipGetLastError();
 }
@@ -814,16 +1112,62 @@ hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
   // four heads at two waves per SIMD.
   constexpr int NBUF = (KT >= kI8 || (KT == kBF16 && HPW == 1)) ? 3 : 2;
   constexpr int WPE = (HPW == 1 && kWide) ? 3 : (kWide ? 2 : 1);
+  using W = ValuWorker<KT, D, HPW, NBUF>;
   const int ratio = a.num_q_heads / a.num_kv_heads;
   if (a.counts) {
     // Whole workgroups must fill the 4 * WPE wave slots of a compute unit.
-    if constexpr ((4 * WPE) % 8 == 0) return launch_balanced<KT, D, HPW, NBUF, WPE, 8>(a, stream);
-    return launch_balanced<KT, D, HPW, NBUF, WPE, 4>(a, stream);
+    if constexpr ((4 * WPE) % 8 == 0) return launch_balanced<W, WPE, 8>(a, stream);
+    return launch_balanced<W, WPE, 4>(a, stream);
   }
   if constexpr (kWide) {
-    if (HPW == 1 || ratio > 4 * HPW) return launch_variant<KT, D, HPW, NBUF, WPE, 8>(a, stream);
+    if (HPW == 1 || ratio > 4 * HPW) return launch_variant<W, WPE, 8>(a, HPW, stream);
   }
-  return launch_variant<KT, D, HPW, NBUF, WPE, 4>(a, stream);
+  return launch_variant<W, WPE, 4>(a, HPW, stream);
+}
+
+// MFMA flavour: one wave per (K/V head, up to 16 query heads).
+// Tuned on MI355X (bf16, head_dim 128, GQA and long-context batches): three
+// register buffers (two blocks in flight) at two waves per SIMD; four
+// buffers changed nothing.  Fixed partitions run in four-wave workgroups,
+// whose finer grain shortened the long-context batch by 6%; the balanced
+// split keeps eight waves (all K/V heads of a block in one workgroup).
+#ifndef KVD_MFMA_NBUF
+#define KVD_MFMA_NBUF 3
+#endif
+#ifndef KVD_MFMA_WPE
+#define KVD_MFMA_WPE 2
+#endif
+#ifndef KVD_MFMA_WG_FIXED
+#define KVD_MFMA_WG_FIXED 4
+#endif
+#ifndef KVD_MFMA_WG_BALANCED
+#define KVD_MFMA_WG_BALANCED 8
+#endif
+constexpr int kMfmaNbuf = KVD_MFMA_NBUF;
+constexpr int kMfmaWpe = KVD_MFMA_WPE;
+
+template <int D>
+hipError_t launch_mfma(const PagedLaunch& a, hipStream_t stream) {
+  using W = MfmaWorker<D, kMfmaNbuf>;
+  const int ratio = a.num_q_heads / a.num_kv_heads;
+  const int hpw = ratio < 16 ? ratio : 16;
+  if (a.counts) return launch_balanced<W, kMfmaWpe, KVD_MFMA_WG_BALANCED>(a, stream);
+  return launch_variant<W, kMfmaWpe, KVD_MFMA_WG_FIXED>(a, hpw, stream);
+}
+
+// Which flavour runs: the MFMA one for bf16 caches with groups of 4 to 16
+// query heads (or multiples of 16), where the VALU flavour's per-head work
+// makes it ALU-bound (VALU busy 74% of the long-context kernel); groups of 1
+// or 2 heads leave most of the MFMA idle, and the VALU flavour measured
+// faster there (MHA batch 188 against 193-199 us).  KVD_PAGED_KERNEL=valu
+// selects the VALU flavour for every group size (for comparisons).
+bool mfma_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("KVD_PAGED_KERNEL");
+    v = (e && strcmp(e, "valu") == 0) ? 0 : 1;
+  }
+  return v == 1;
 }
 
 // Groups of more than 4 query heads are split over ratio / 4 wavefronts of the
@@ -859,7 +1203,16 @@ int max_partition_blocks() { return kMaxPartitionBlocks; }
 
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream) {
   if (a.int8) return a.fp8 ? launch_by_dim<kF8>(a, stream) : launch_by_dim<kI8>(a, stream);
-  return a.bf16 ? launch_by_dim<kBF16>(a, stream) : launch_by_dim<kF32>(a, stream);
+  if (!a.bf16) return launch_by_dim<kF32>(a, stream);
+  const int ratio = a.num_q_heads / a.num_kv_heads;
+  if (mfma_enabled() && ratio >= 4 && (ratio <= 16 || ratio % 16 == 0)) {
+    switch (a.head_dim) {
+      case 32: return launch_mfma<32>(a, stream);
+      case 64: return launch_mfma<64>(a, stream);
+      default: return launch_mfma<128>(a, stream);
+    }
+  }
+  return launch_by_dim<kBF16>(a, stream);
 }
 
 }  // namespace kvd

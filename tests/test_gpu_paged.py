@@ -104,6 +104,11 @@ DECODE_CASES = [
     # 8-wave workgroup
     ("r12-balanced", dict(B=3, H_q=24, H_kv=2, d=64, lens=[257, 40, 1600], pt=0)),
     ("r12-split256", dict(B=3, H_q=24, H_kv=2, d=64, lens=[257, 40, 1600], pt=256)),
+    # head_dim 32 with groups of 4 and 8 (MFMA flavour), a group of 24 (the
+    # VALU flavour: more than 16 heads and not a multiple of 16)
+    ("r4-d32", dict(B=3, H_q=8, H_kv=2, d=32, lens=[1, 300, 1025], pt=0)),
+    ("r8-d32-pt64", dict(B=2, H_q=16, H_kv=2, d=32, lens=[70, 513], pt=64)),
+    ("r24-valu", dict(B=2, H_q=48, H_kv=2, d=128, lens=[900, 33], pt=0)),
 ]
 
 

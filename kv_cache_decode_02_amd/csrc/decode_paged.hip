@@ -592,7 +592,8 @@ struct ValuWorker {
   }
 };
 
-// MFMA flavour (bf16 caches, groups of up to 16 query heads per wave).  For
+// MFMA flavour (bf16 and one-byte caches, groups of up to 16 query heads per
+// wave).  For
 // one 16-token block of K/V head g and the wave's query heads:
 //   scores  S^T[token][head] = K_blk[16 x D] . Q^T[D x 16]: D/32 MFMA
 //           16x16x32; K rows go straight from HBM into the A operand (lane
@@ -618,81 +619,157 @@ struct ValuWorker {
 // Per block and wave this is D/32 + D/8 MFMAs and ~50 VALU instructions
 // for all heads of the group, against ~300 VALU instructions per 4 heads in
 // the VALU flavour.
-template <int D>
+// One-byte caches (INT8, FP8 E4M3) use fp16 MFMAs: the codes are widened in
+// registers to fp16 (INT8 as kI8Bias + code by byte permutes, its offsets
+// removed from the scores and the accumulators; FP8 exactly), the queries
+// carry the per-channel K scales and the weights the per-token V scales, and
+// the weights enter once as fp16 (as in the VALU flavour), since the codes
+// themselves are coarser than that.
+template <int KT, int D>
 struct MShape {
-  static constexpr int KS = D / 32;   // K-steps of the scores
-  static constexpr int NT = D / 16;   // 16-dimension column tiles of the output
-  static constexpr int C = D / 8;     // 16-byte chunks per row of one K/V head
-  static constexpr int ROWB = 2 * D;  // bytes per row of one K/V head
+  static constexpr int EB = KT == kBF16 ? 2 : 1;  // bytes per stored element
+  static constexpr int KS = D / 32;               // K-steps of the scores
+  static constexpr int NL = D * EB / 64;          // 16-byte loads per row per lane (each of K, V)
+  static constexpr int NT = D / 16;               // 16-dimension column tiles of the output
+  static constexpr int C = D / 8;                 // 16-byte chunks per LDS row (16-bit values)
+  static constexpr int ROWB = 2 * D;              // LDS bytes per row (bf16 or fp16 values)
+  static constexpr int GROWB = D * EB;            // cache bytes per row of one K/V head
+  static_assert(NL >= 1, "head_dim too small for this element kind");
   // Chunk position of chunk c of LDS row r (XOR swizzle).
   static __device__ __forceinline__ int pos(int r, int c) { return c ^ ((r * D / 128) % C); }
+  // First dimension of the 8 that lane group G supplies in K-step s: bf16
+  // rows give 8 consecutive dimensions per K-step; one-byte rows give 16
+  // consecutive codes per load, i.e. two K-steps.
+  static __device__ __forceinline__ int kdim(int s, int G) {
+    return EB == 2 ? 32 * s + 8 * G : 64 * (s >> 1) + 16 * G + 8 * (s & 1);
+  }
 };
 
-template <int D>
+template <int KT, int D>
 struct MFrag {
-  uint32_t k[MShape<D>::KS][4];
-  uint32_t v[MShape<D>::KS][4];
+  uint32_t k[MShape<KT, D>::NL][4];
+  uint32_t v[MShape<KT, D>::NL][4];
+  float vs[1];  // one-byte caches: V scale of token 4 G + lane % 4
 };
 
-// Rows of K/V head g for the lane: token i of the block, dimensions
-// 32 s + 8 G .. + 7 for each K-step s; rows at or past nvalid read as zeros.
-template <int D>
-__device__ __forceinline__ void mfma_rows(MFrag<D>& f, const uint32_t* kbase, const uint32_t* vbase,
-                                          const PagedLaunch& a, int lane, int g, int nvalid) {
-  const int tok_bytes = a.num_kv_heads * MShape<D>::ROWB;
+// Rows of K/V head g for the lane (G, i): token i of the block, its 16-byte
+// loads p covering bytes 64 p + 16 G .. + 15 of the head's row; rows at or
+// past nvalid read as zeros.  One-byte caches also fetch the V scale of
+// token 4 G + i % 4 (sbase: the block's [16][H_kv] scales).
+template <int KT, int D>
+__device__ __forceinline__ void mfma_rows(MFrag<KT, D>& f, const void* kbase, const void* vbase,
+                                          const PagedLaunch& a, int lane, int g, int nvalid,
+                                          const float* sbase = nullptr) {
+  using S = MShape<KT, D>;
+  const int tok_bytes = a.num_kv_heads * S::GROWB;
   const int bytes = nvalid * tok_bytes;
   const BufRsrc rk = make_rsrc(kbase, bytes);
   const BufRsrc rv = make_rsrc(vbase, bytes);
-  const uint32_t off = static_cast<uint32_t>((lane & 15) * tok_bytes + g * MShape<D>::ROWB +
-                                             16 * (lane >> 4));
+  const int G = lane >> 4;
+  const uint32_t off = static_cast<uint32_t>((lane & 15) * tok_bytes + g * S::GROWB + 16 * G);
 #pragma unroll
-  for (int s = 0; s < MShape<D>::KS; ++s) {
-    buffer_load_words<4>(f.k[s], rk, off + 64 * s);
-    buffer_load_words<4>(f.v[s], rv, off + 64 * s);
+  for (int p = 0; p < S::NL; ++p) {
+    buffer_load_words<4>(f.k[p], rk, off + 64 * p);
+    buffer_load_words<4>(f.v[p], rv, off + 64 * p);
+  }
+  if constexpr (KT != kBF16) {
+    // One load: lane (G, i) fetches the scale of token 4 G + i % 4; the
+    // quad broadcasts in mfma_block hand each lane all four.
+    const BufRsrc rs = make_rsrc(sbase, nvalid * a.num_kv_heads * 4);
+    f.vs[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rs, static_cast<uint32_t>(((4 * G + (lane & 3)) * a.num_kv_heads + g) * 4), 0, 0));
   }
 }
 
-template <int D>
-__device__ __forceinline__ void mfma_block_rows(MFrag<D>& f, const PagedLaunch& a, int lane, int g,
-                                                int blk, int nvalid) {
-  const size_t words = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens *
-                       a.num_kv_heads * (D / 2);
-  mfma_rows<D>(f, static_cast<const uint32_t*>(a.k_cache) + words,
-               static_cast<const uint32_t*>(a.v_cache) + words, a, lane, g, nvalid);
+template <int KT, int D>
+__device__ __forceinline__ void mfma_block_rows(MFrag<KT, D>& f, const PagedLaunch& a, int lane,
+                                                int g, int blk, int nvalid) {
+  using S = MShape<KT, D>;
+  const size_t row0 = static_cast<size_t>(nvalid > 0 ? blk : 0) * kBlockTokens;
+  const size_t bytes = row0 * a.num_kv_heads * S::GROWB;
+  mfma_rows<KT, D>(f, static_cast<const unsigned char*>(a.k_cache) + bytes,
+                   static_cast<const unsigned char*>(a.v_cache) + bytes, a, lane, g, nvalid,
+                   KT == kBF16 ? nullptr : a.v_scale + row0 * a.num_kv_heads);
 }
 
 template <int D>
 struct MState {
-  f32x4_t acc[MShape<D>::NT];  // O^T: head lane % 16, dims 16 t + 4 (lane / 16) + j
-  float m;                     // reference max of the lane's head (log2 units)
-  float l;                     // the lane's share of the weight sum
+  f32x4_t acc[D / 16];  // O^T: head lane % 16, dims 16 t + 4 (lane / 16) + j
+  float m;              // reference max of the lane's head (log2 units)
+  float l;              // the lane's share of the weight sum
+  float vb;             // INT8: the lane's share of the weights that met biased codes
 };
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+
+// Sixteen one-byte codes (four words) as eight fp16 pairs of neighbouring
+// codes: INT8 as biased numbers kI8Bias + code (byte permutes), FP8 as the
+// exact E4M3 values.
+template <int KT>
+__device__ __forceinline__ void widen16(const uint32_t (&w)[4], uint32_t (&o)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (KT == kI8) {
+      const uint32_t u = w[k] ^ kSignBits;
+      o[2 * k] = biased_pair(u, 0);
+      o[2 * k + 1] = biased_pair(u, 1);
+    } else {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
+      o[2 * k] = pack_f16x2_int(lo[0], lo[1]);
+      o[2 * k + 1] = pack_f16x2_int(hi[0], hi[1]);
+    }
+  }
+}
+
 // One block through the online softmax: tokens [nskip, nvalid) count.  `lds`
-// is the wave's LDS slice (16 rows of one K/V head).
-template <int D>
-__device__ __forceinline__ void mfma_block(const MFrag<D>& f, const uint32_t (&q)[MShape<D>::KS][4],
-                                           unsigned char* lds, int lane, int nskip, int nvalid,
-                                           float sl2, MState<D>& st) {
-  using S = MShape<D>;
+// is the wave's LDS slice (16 rows of one K/V head as 16-bit values).
+// q: the B operand of the scores (bf16, or fp16 scaled queries); qb: INT8's
+// score offset of the lane's head.
+template <int KT, int D>
+__device__ __forceinline__ void mfma_block(const MFrag<KT, D>& f, const uint32_t (&q)[D / 32][4],
+                                           float qb, unsigned char* lds, int lane, int nskip,
+                                           int nvalid, float sl2, MState<D>& st) {
+  using S = MShape<KT, D>;
   const int G = lane >> 4, i = lane & 15;
   f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KT == kBF16) {
 #pragma unroll
-  for (int s = 0; s < S::KS; ++s)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-        as_bf16x8(f.k[s][0], f.k[s][1], f.k[s][2], f.k[s][3]),
-        as_bf16x8(q[s][0], q[s][1], q[s][2], q[s][3]), sc, 0, 0, 0);
-  // V rows into the LDS slice: row i, chunk 4 s + G.
+    for (int s = 0; s < S::KS; ++s)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          as_bf16x8(f.k[s][0], f.k[s][1], f.k[s][2], f.k[s][3]),
+          as_bf16x8(q[s][0], q[s][1], q[s][2], q[s][3]), sc, 0, 0, 0);
+    // V rows into the LDS slice: row i, chunk 4 s + G.
 #pragma unroll
-  for (int s = 0; s < S::KS; ++s)
-    *reinterpret_cast<uint4*>(lds + i * S::ROWB + S::pos(i, 4 * s + G) * 16) =
-        make_uint4(f.v[s][0], f.v[s][1], f.v[s][2], f.v[s][3]);
+    for (int s = 0; s < S::KS; ++s)
+      *reinterpret_cast<uint4*>(lds + i * S::ROWB + S::pos(i, 4 * s + G) * 16) =
+          make_uint4(f.v[s][0], f.v[s][1], f.v[s][2], f.v[s][3]);
+  } else {
+#pragma unroll
+    for (int p = 0; p < S::NL; ++p) {
+      uint32_t kw[8], vw[8];
+      widen16<KT>(f.k[p], kw);
+      widen16<KT>(f.v[p], vw);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int s = 2 * p + h;
+        const uint4 ka = make_uint4(kw[4 * h], kw[4 * h + 1], kw[4 * h + 2], kw[4 * h + 3]);
+        const uint4 qa = make_uint4(q[s][0], q[s][1], q[s][2], q[s][3]);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, ka),
+                                                    __builtin_bit_cast(f16x8_t, qa), sc, 0, 0, 0);
+        // fp16 V values: row i, chunk 8 p + 2 G + h.
+        *reinterpret_cast<uint4*>(lds + i * S::ROWB + S::pos(i, 8 * p + 2 * G + h) * 16) =
+            make_uint4(vw[4 * h], vw[4 * h + 1], vw[4 * h + 2], vw[4 * h + 3]);
+      }
+    }
+  }
   float z[4];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = 4 * G + j;
-    z[j] = (t >= nskip && t < nvalid) ? sc[j] * sl2 : -INFINITY;
+    z[j] = (t >= nskip && t < nvalid) ? (sc[j] + qb) * sl2 : -INFINITY;
     mx = fmaxf(mx, z[j]);
   }
   mx = row_max4(mx);
@@ -701,6 +778,7 @@ __device__ __forceinline__ void mfma_block(const MFrag<D>& f, const uint32_t (&q
     const float mn = up ? mx : st.m;
     const float alpha = exp2_fast(st.m - mn);
     st.l *= alpha;
+    if constexpr (KT == kI8) st.vb *= alpha;
 #pragma unroll
     for (int t = 0; t < S::NT; ++t)
 #pragma unroll
@@ -711,29 +789,62 @@ __device__ __forceinline__ void mfma_block(const MFrag<D>& f, const uint32_t (&q
 #pragma unroll
   for (int j = 0; j < 4; ++j) p[j] = exp2_fast(z[j] - st.m);
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  const uint32_t h0 = pack_bf16x2(p[0], p[1]), h1 = pack_bf16x2(p[2], p[3]);
-  const uint32_t r0 = pack_bf16x2(p[0] - bf16_lo(h0), p[1] - bf16_hi(h0));
-  const uint32_t r1 = pack_bf16x2(p[2] - bf16_lo(h1), p[3] - bf16_hi(h1));
-  const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h0, h1));
-  const s16x4_t pr = __builtin_bit_cast(s16x4_t, make_uint2(r0, r1));
   // Transpose reads: lane (G, i) addresses row 4 G + i / 4, dimensions
   // 16 t + 4 (i % 4) .. + 3, and receives dimension 16 t + i of rows
   // 4 G .. 4 G + 3.
   const int rr = 4 * G + (i >> 2);
   unsigned char* rbase = lds + rr * S::ROWB + 8 * (i & 1);
+  if constexpr (KT == kBF16) {
+    const uint32_t h0 = pack_bf16x2(p[0], p[1]), h1 = pack_bf16x2(p[2], p[3]);
+    const uint32_t r0 = pack_bf16x2(p[0] - bf16_lo(h0), p[1] - bf16_hi(h0));
+    const uint32_t r1 = pack_bf16x2(p[2] - bf16_lo(h1), p[3] - bf16_hi(h1));
+    const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h0, h1));
+    const s16x4_t pr = __builtin_bit_cast(s16x4_t, make_uint2(r0, r1));
 #pragma unroll
-  for (int t = 0; t < S::NT; ++t) {
-    const int c = 2 * t + ((i & 3) >> 1);
-    const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(rbase + S::pos(rr, c) * 16));
-    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, st.acc[t], 0, 0, 0);
-    st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pr, st.acc[t], 0, 0, 0);
+    for (int t = 0; t < S::NT; ++t) {
+      const int c = 2 * t + ((i & 3) >> 1);
+      const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(rbase + S::pos(rr, c) * 16));
+      st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, st.acc[t], 0, 0, 0);
+      st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pr, st.acc[t], 0, 0, 0);
+    }
+  } else {
+    // One-byte caches: the weights times the tokens' V scales meet the
+    // widened codes (p * (s * code) = (p * s) * code) as fp16.
+    // quad_perm broadcasts: every lane of a quad takes lane j's scale
+    const float s0 = dpp_move<0x00>(f.vs[0]), s1 = dpp_move<0x55>(f.vs[0]);
+    const float s2 = dpp_move<0xAA>(f.vs[0]), s3 = dpp_move<0xFF>(f.vs[0]);
+    const uint32_t w0 = pack_f16x2(p[0] * s0, p[1] * s1);
+    const uint32_t w1 = pack_f16x2(p[2] * s2, p[3] * s3);
+    if constexpr (KT == kI8) st.vb = dot2_f16(w1, kF16OnePair, dot2_f16(w0, kF16OnePair, st.vb));
+    const f16x4_t pw = __builtin_bit_cast(f16x4_t, make_uint2(w0, w1));
+#pragma unroll
+    for (int t = 0; t < S::NT; ++t) {
+      const int c = 2 * t + ((i & 3) >> 1);
+      const s16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(rbase + S::pos(rr, c) * 16));
+      st.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, vt), pw,
+                                                        st.acc[t], 0, 0, 0);
+    }
   }
 }
 
-template <int D, int NBUF>
+// INT8: takes the value bias out of the accumulators (the weights of all 16
+// tokens of a block meet every output column, so the bias of a column is
+// kI8Bias times the head's whole weight sum, gathered over the four lanes).
+template <int D>
+__device__ __forceinline__ void mfma_unbias(MState<D>& st) {
+  const float vb = row_sum4(st.vb);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.acc[t][j] = fmaf(-kI8Bias, vb, st.acc[t][j]);
+  st.vb = 0.f;
+}
+
+template <int KT, int D, int NBUF>
 struct MfmaWorker {
-  using S = MShape<D>;
+  using S = MShape<KT, D>;
   static constexpr int kLdsPerWave = 16 * S::ROWB;
   static constexpr long long kEvenXcdShare = 1060;
   static __device__ __forceinline__ int heads_per_wave(int ratio) { return ratio < 16 ? ratio : 16; }
@@ -753,21 +864,64 @@ struct MfmaWorker {
     }
   }
 
-  static __device__ __forceinline__ void empty(const PagedLaunch& a, int lane, size_t slot0,
-                                               size_t P) {
-    MState<D> st;
+  static __device__ __forceinline__ void reset(MState<D>& st) {
 #pragma unroll
     for (int t = 0; t < S::NT; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     st.m = kMinusBig;
     st.l = 0.f;
+    st.vb = 0.f;
+  }
+
+  static __device__ __forceinline__ void empty(const PagedLaunch& a, int lane, size_t slot0,
+                                               size_t P) {
+    MState<D> st;
+    reset(st);
     const int ratio = a.num_q_heads / a.num_kv_heads;
     write(a, lane, slot0, P, heads_per_wave(ratio), st);
   }
 
+  // Queries of heads h0 .. h0 + nheads - 1 as the B operand (head lane % 16,
+  // zero past the wave's heads).  bf16 caches: the bf16 queries.  One-byte
+  // caches: q times K/V head g's per-channel K scales, rounded to fp16
+  // (q . (s * code) = (q * s) . code); INT8 also returns the score offset
+  // -kI8Bias * (sum of the head's scaled query), from the same fp16 values.
+  static __device__ __forceinline__ float load_q(const PagedLaunch& a, int lane, int b, int h0,
+                                                 int g, int nheads, uint32_t (&q)[D / 32][4]) {
+    const int G = lane >> 4, i = lane & 15;
+    const bool live = i < nheads;
+    const uint32_t* qrow = static_cast<const uint32_t*>(a.q) +
+                           (static_cast<size_t>(b) * a.num_q_heads + h0 + (live ? i : 0)) * (D / 2);
+    float qs = 0.f;
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) {
+      const int d0 = S::kdim(s, G);
+      uint32_t w[4];
+      load_words<4>(w, qrow + d0 / 2);
+      if constexpr (KT == kBF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[s][k] = live ? w[k] : 0u;
+      } else {
+        const float* ks = a.k_scale + static_cast<size_t>(g) * D + d0;
+        const float4 s0 = *reinterpret_cast<const float4*>(ks);
+        const float4 s1 = *reinterpret_cast<const float4*>(ks + 4);
+        q[s][0] = pack_f16x2(bf16_lo(w[0]) * s0.x, bf16_hi(w[0]) * s0.y);
+        q[s][1] = pack_f16x2(bf16_lo(w[1]) * s0.z, bf16_hi(w[1]) * s0.w);
+        q[s][2] = pack_f16x2(bf16_lo(w[2]) * s1.x, bf16_hi(w[2]) * s1.y);
+        q[s][3] = pack_f16x2(bf16_lo(w[3]) * s1.z, bf16_hi(w[3]) * s1.w);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (!live) q[s][k] = 0u;
+          qs = dot2_f16(q[s][k], kF16OnePair, qs);
+        }
+      }
+    }
+    return KT == kI8 ? -kI8Bias * row_sum4(qs) : 0.f;
+  }
+
   // Blocks [j_begin, j_end) of sequence b, K/V head g, query heads h0 ..;
   // tokens before t_start or at or past t_end carry no weight.  With
-  // `fused` the range ends at position t_end - 1, which is taken from
-  // k_new / v_new as a one-token block after the others, and with
+  // `fused` (bf16 caches) the range ends at position t_end - 1, which is
+  // taken from k_new / v_new as a one-token block after the others, and with
   // `write_new` the wave also stores head g's part of those rows into their
   // cache slot.
   static __device__ __forceinline__ void unit(const PagedLaunch& a, int lane, unsigned char* lds,
@@ -777,28 +931,15 @@ struct MfmaWorker {
     const int ratio = a.num_q_heads / a.num_kv_heads;
     const int nheads = heads_per_wave(ratio);
     const int G = lane >> 4, i = lane & 15;
-    // Queries as the B operand: head h0 + i (zero past the wave's heads).
     uint32_t q[S::KS][4];
-    {
-      const uint32_t* qrow = static_cast<const uint32_t*>(a.q) +
-                             (static_cast<size_t>(b) * a.num_q_heads + h0 + (i < nheads ? i : 0)) *
-                                 (D / 2);
-#pragma unroll
-      for (int s = 0; s < S::KS; ++s) {
-        load_words<4>(q[s], qrow + (32 * s + 8 * G) / 2);
-        if (i >= nheads) q[s][0] = q[s][1] = q[s][2] = q[s][3] = 0u;
-      }
-    }
+    const float qb = load_q(a, lane, b, h0, g, nheads, q);
     MState<D> st;
-#pragma unroll
-    for (int t = 0; t < S::NT; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    st.m = kMinusBig;
-    st.l = 0.f;
+    reset(st);
     const int t_last = t_end - 1;
     if (fused) t_end = t_last;
     const float sl2 = a.scale * kLog2e;
     const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
-    MFrag<D> buf[NBUF];
+    MFrag<KT, D> buf[NBUF];
 
     for (int c0 = j_begin; c0 < j_end; c0 += kMaxPartitionBlocks) {
       const int nblk = min(kMaxPartitionBlocks, j_end - c0);
@@ -813,7 +954,7 @@ struct MfmaWorker {
       for (int s0 = 0; s0 < NBUF; ++s0) {
         int nv;
         const int blk = block_of(s0, nv);
-        mfma_block_rows<D>(buf[s0], a, lane, g, blk, nv);
+        mfma_block_rows<KT, D>(buf[s0], a, lane, g, blk, nv);
       }
       for (int base = 0; base < nblk; base += NBUF) {
 #pragma unroll
@@ -822,34 +963,37 @@ struct MfmaWorker {
           if (jj < nblk) {
             int nv;
             block_of(jj, nv);
-            mfma_block<D>(buf[s0], q, lds, lane, max(0, t_start - (c0 + jj) * kBlockTokens), nv,
-                          sl2, st);
+            mfma_block<KT, D>(buf[s0], q, qb, lds, lane,
+                              max(0, t_start - (c0 + jj) * kBlockTokens), nv, sl2, st);
           }
           int nv;
           const int blk = block_of(jj + NBUF, nv);
-          mfma_block_rows<D>(buf[s0], a, lane, g, blk, nv);
+          mfma_block_rows<KT, D>(buf[s0], a, lane, g, blk, nv);
         }
       }
+      if constexpr (KT == kI8) mfma_unbias(st);
     }
-    if (fused) {
-      const int blk = wave_uniform(trow[t_last / kBlockTokens]);
-      if (blk >= 0 && blk < a.num_blocks) {
-        const size_t row_words = static_cast<size_t>(a.num_kv_heads) * (D / 2);
-        const size_t src = static_cast<size_t>(b) * row_words;
-        MFrag<D> f;
-        mfma_rows<D>(f, static_cast<const uint32_t*>(a.k_new) + src,
-                     static_cast<const uint32_t*>(a.v_new) + src, a, lane, g, 1);
-        mfma_block<D>(f, q, lds, lane, 0, 1, sl2, st);
-        if (write_new && i == 0) {
-          // Lanes (G, 0) hold dimensions 32 s + 8 G .. + 7 of the new rows.
-          const size_t dst = (static_cast<size_t>(blk) * kBlockTokens + t_last % kBlockTokens) *
-                                 row_words + g * (D / 2);
-          uint32_t* kd = static_cast<uint32_t*>(const_cast<void*>(a.k_cache)) + dst;
-          uint32_t* vd = static_cast<uint32_t*>(const_cast<void*>(a.v_cache)) + dst;
+    if constexpr (KT == kBF16) {
+      if (fused) {
+        const int blk = wave_uniform(trow[t_last / kBlockTokens]);
+        if (blk >= 0 && blk < a.num_blocks) {
+          const size_t row_words = static_cast<size_t>(a.num_kv_heads) * (D / 2);
+          const size_t src = static_cast<size_t>(b) * row_words;
+          MFrag<KT, D> f;
+          mfma_rows<KT, D>(f, static_cast<const uint32_t*>(a.k_new) + src,
+                           static_cast<const uint32_t*>(a.v_new) + src, a, lane, g, 1);
+          mfma_block<KT, D>(f, q, qb, lds, lane, 0, 1, sl2, st);
+          if (write_new && i == 0) {
+            // Lanes (G, 0) hold dimensions 32 s + 8 G .. + 7 of the new rows.
+            const size_t dst = (static_cast<size_t>(blk) * kBlockTokens + t_last % kBlockTokens) *
+                                   row_words + g * (D / 2);
+            uint32_t* kd = static_cast<uint32_t*>(const_cast<void*>(a.k_cache)) + dst;
+            uint32_t* vd = static_cast<uint32_t*>(const_cast<void*>(a.v_cache)) + dst;
 #pragma unroll
-          for (int s = 0; s < S::KS; ++s) {
-            store_words<4>(kd + (32 * s + 8 * G) / 2, f.k[s]);
-            store_words<4>(vd + (32 * s + 8 * G) / 2, f.v[s]);
+            for (int s = 0; s < S::KS; ++s) {
+              store_words<4>(kd + (32 * s + 8 * G) / 2, f.k[s]);
+              store_words<4>(vd + (32 * s + 8 * G) / 2, f.v[s]);
+            }
           }
         }
       }
@@ -1143,16 +1287,28 @@ hipError_t launch_typed(const PagedLaunch& a, hipStream_t stream) {
 #ifndef KVD_MFMA_WG_BALANCED
 #define KVD_MFMA_WG_BALANCED 8
 #endif
+#ifndef KVD_MFMA_NBUF_BYTE
+#define KVD_MFMA_NBUF_BYTE 3
+#endif
+#ifndef KVD_MFMA_WPE_BYTE
+#define KVD_MFMA_WPE_BYTE 2
+#endif
 constexpr int kMfmaNbuf = KVD_MFMA_NBUF;
 constexpr int kMfmaWpe = KVD_MFMA_WPE;
 
-template <int D>
+template <int KT, int D>
 hipError_t launch_mfma(const PagedLaunch& a, hipStream_t stream) {
-  using W = MfmaWorker<D, kMfmaNbuf>;
+  constexpr int NBUF = KT == kBF16 ? kMfmaNbuf : KVD_MFMA_NBUF_BYTE;
+  constexpr int WPE = KT == kBF16 ? kMfmaWpe : KVD_MFMA_WPE_BYTE;
+  using W = MfmaWorker<KT, D, NBUF>;
   const int ratio = a.num_q_heads / a.num_kv_heads;
   const int hpw = ratio < 16 ? ratio : 16;
-  if (a.counts) return launch_balanced<W, kMfmaWpe, KVD_MFMA_WG_BALANCED>(a, stream);
-  return launch_variant<W, kMfmaWpe, KVD_MFMA_WG_FIXED>(a, hpw, stream);
+  if (a.counts) {
+    if constexpr ((4 * WPE) % KVD_MFMA_WG_BALANCED == 0)
+      return launch_balanced<W, WPE, KVD_MFMA_WG_BALANCED>(a, stream);
+    return launch_balanced<W, WPE, 4>(a, stream);
+  }
+  return launch_variant<W, WPE, KVD_MFMA_WG_FIXED>(a, hpw, stream);
 }
 
 // Which flavour runs: the MFMA one for bf16 caches with groups of 4 to 16
@@ -1202,17 +1358,23 @@ bool paged_supported(int head_dim, int ratio, bool /*bf16*/) {
 int max_partition_blocks() { return kMaxPartitionBlocks; }
 
 hipError_t launch_paged_partials(const PagedLaunch& a, hipStream_t stream) {
-  if (a.int8) return a.fp8 ? launch_by_dim<kF8>(a, stream) : launch_by_dim<kI8>(a, stream);
-  if (!a.bf16) return launch_by_dim<kF32>(a, stream);
   const int ratio = a.num_q_heads / a.num_kv_heads;
-  if (mfma_enabled() && ratio >= 4 && (ratio <= 16 || ratio % 16 == 0)) {
+  const bool mfma = mfma_enabled() && ratio >= 4 && (ratio <= 16 || ratio % 16 == 0);
+  if (a.int8) {
+    if (mfma && (a.head_dim == 64 || a.head_dim == 128)) {
+      if (a.fp8) return a.head_dim == 64 ? launch_mfma<kF8, 64>(a, stream) : launch_mfma<kF8, 128>(a, stream);
+      return a.head_dim == 64 ? launch_mfma<kI8, 64>(a, stream) : launch_mfma<kI8, 128>(a, stream);
+    }
+    return a.fp8 ? launch_by_dim<kF8>(a, stream) : launch_by_dim<kI8>(a, stream);
+  }
+  if (!a.bf16) return launch_by_dim<kF32>(a, stream);
+  if (mfma) {
     switch (a.head_dim) {
-      case 32: return launch_mfma<32>(a, stream);
-      case 64: return launch_mfma<64>(a, stream);
-      default: return launch_mfma<128>(a, stream);
+      case 32: return launch_mfma<kBF16, 32>(a, stream);
+      case 64: return launch_mfma<kBF16, 64>(a, stream);
+      default: return launch_mfma<kBF16, 128>(a, stream);
     }
   }
   return launch_by_dim<kBF16>(a, stream);
 }
-
 }  // namespace kvd

@@ -114,6 +114,10 @@ DECODE_CASES = [
     ("r2-d64", dict(B=3, H_q=8, H_kv=4, d=64, lens=[33, 999, 1], pt=0)),
     ("r8-d128", dict(B=2, H_q=64, H_kv=8, d=128, lens=[2500, 300], pt=0)),
     ("mqa-d32", dict(B=2, H_q=4, H_kv=1, d=32, lens=[129, 640], pt=64)),
+    # head_dim 64 on the MFMA flavour: a group of 4, and one of 16 over long
+    # fixed partitions
+    ("r4-d64", dict(B=3, H_q=8, H_kv=2, d=64, lens=[70, 1500, 3000], pt=0)),
+    ("r16-d64-pt512", dict(B=2, H_q=16, H_kv=1, d=64, lens=[1200, 5000], pt=512)),
     # history codes over every finite magnitude 0x00 .. 0x7E (values up to 448
     # times the scale), both signs
     ("gqa-r4-full-range", dict(B=4, H_q=32, H_kv=8, d=128, lens=[17, 700, 2049, 4000], pt=0,

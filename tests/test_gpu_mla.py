@@ -182,3 +182,54 @@ def test_mla_full_size_sampled(fused):
         ref = oracle.mla_decode(oracle.to_f64(inp.q[b], "bf16"), C, 512, scale)
         assert_contract(got[b], ref, f"mla full b={b}")
     log("mla full: ok")
+
+
+def _bf16_bits(x):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def _plant(inp, b, rows):
+    """rows: {position: z} -- the latent row of sequence b at that position
+    becomes a multiple of query head 0's vector, so that head 0's score there
+    is about z (log2 units, scale and log2(e) included) above that of a
+    near-zero row.  The positions precede the appended one."""
+    scale = kvd.mla_default_scale()
+    q0 = oracle.to_f64(inp.q[b, 0], "bf16")
+    unit = q0 / (scale * np.log2(np.e) * float(q0 @ q0))
+    for t, z in rows.items():
+        assert t < int(inp.seq_lens[b]) - 1
+        blk = int(inp.block_table[b, t // 16])
+        inp.c_pool[blk, t % 16] = _bf16_bits(oracle.to_f64(inp.c_pool[blk, t % 16], "bf16") +
+                                            z * unit)
+
+
+# Scores far above the first tile's maximum in a later tile of the same
+# partition: up to 64 log2 units the weights stay in range in one pass; past
+# that the partition runs a second time with the exact maximum.  A ramp moves
+# head 0's scores up along the whole sequence (one partition of 1024 tokens:
+# 150 log2 units from its first tile to its last).
+SPREAD = [
+    ("spike-40", 0, {0: {40: 40.0, 200: 40.0}, 1: {33: 40.0, 900: 40.0}}),
+    ("spike-100", 64, {0: {40: 100.0, 250: 100.0}, 1: {70: 100.0, 999: 100.0}}),
+    ("ramp-150", 1024, {0: {t: 150.0 * t / 511 for t in range(299)},
+                     1: {t: 150.0 * (t % 512) / 511 for t in range(999)}}),
+]
+
+
+@pytest.mark.parametrize("name,pt,plants", SPREAD, ids=[n for n, _, _ in SPREAD])
+def test_mla_score_spread(name, pt, plants):
+    log(f"mla score spread {name}")
+    inp = make_mla(np.random.default_rng(zlib.crc32(name.encode())), 2, 128, 512, 64,
+                   [300, 1001], std=1 / 24)
+    for b, rows in plants.items():
+        _plant(inp, b, rows)
+    fused, sep = Dev(inp), Dev(inp)
+    out = kvd.decode_attn_mla_append(fused.q, fused.c, fused.c_new[:, 0], fused.table, fused.seq,
+                                     inp.max_seq_len, partition_tokens=pt)
+    two = _step(sep, pt)
+    assert torch.equal(out.view(torch.int16), two.view(torch.int16))
+    got = down_f64(out)
+    assert np.all(np.isfinite(got))
+    rep = assert_contract(got, _ref(inp), name)
+    log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")

@@ -8,37 +8,49 @@
 // ("KV Cache（键值缓存）", 2.2 路线一, the MLA equations and the decoupled-RoPE
 // note; 4 实现要点, MLA needs a kernel that absorbs the up-projection).
 // 128 heads against one shared row is a dense contraction, so both products
-// run on MFMA (bf16 operands, fp32 accumulation).
+// run on MFMA 32x32x16 (bf16 operands, fp32 accumulation).
 //
 // Work decomposition:
-//   workgroup = (sequence b, partition p, group of 64 query heads), 8 waves
-//   (two per SIMD).  Waves w and w + 4 form a pair that owns 16 heads: for
-//   the scores each takes one half of the 576-wide K dimension and the two
-//   partial score blocks are added through LDS; for the output each takes
-//   one half of the 512 latent columns.  No MFMA work is duplicated and a
-//   wave needs 64 accumulator registers, not 128, which leaves room for two
-//   waves per SIMD.
-//   The partition's tokens are processed in tiles of 32 (two 16-token
-//   blocks).  Each tile is loaded once from HBM by the whole workgroup
-//   (buffer loads through the block table, rows past the sequence end read
-//   as zeros), stored token-major in LDS and read by all 8 waves.  The two
-//   head groups of one (sequence, partition) are launched 8 workgroups
-//   apart, so they run on the same XCD and the second reads the tile from L2.
-//   Scores:  S^T[token][head] = C_tile[32 x 288] . Q~^T[288 x 16] per wave
-//            as 2 x 9 MFMA 16x16x32; Q~ stays in registers as the B operand.
-//            Every lane ends with one head and 8 tokens.
+//   workgroup = (sequence b, partition p, group of 64 query heads), 8 waves,
+//   two blocks of 32 heads.  The waves specialise:
+//     score waves 0-3   (head block w & 1, K half w >> 1): partial scores
+//                       over their half of the 576-wide rows, Q~ held in
+//                       registers; the two halves are added through LDS and
+//                       both waves of a block take the same softmax
+//                       decisions; each writes the weights of one 16-token
+//                       half of the tile to LDS;
+//     value waves 4-7   (head block w & 1, column half (w - 4) >> 1): the
+//                       unnormalised output of 32 heads x 256 latent columns
+//                       in registers, fed by those weights.
+//   With the usual placement of wave w on SIMD w % 4 every SIMD holds one
+//   score wave and one value wave, so the softmax arithmetic of the one
+//   overlaps the matrix products of the other.  Every LDS fragment of the
+//   tile feeds the MFMAs of 32 heads.
+//   Tokens come in tiles of 32 (two 16-token blocks), loaded once per
+//   workgroup through the block table (rows past the sequence end read as
+//   zeros), stored token-major in LDS and shared by all 8 waves.  The two head
+//   groups of one (sequence, partition) are launched 8 workgroups apart, so
+//   they run on the same XCD and the second reads the tiles from L2.
+//   Scores:  S^T[token][head] = C_tile[32 x 288] . Q~^T[288 x 32] per score
+//            wave, 18 MFMAs; every lane ends with one head and 16 tokens.
 //   Softmax: online per head with a lazily raised reference max (raised only
-//            when a score exceeds it by more than kRaise log2 units); weights
-//            enter the MFMA as a bf16 value plus its bf16 remainder, the
-//            running sum takes them in fp32.  Both waves of a pair compute the
-//            same weights from the same summed scores.
-//   Output:  O^T[256 x 16] += C_tile^T[256 x 32] . P^T[32 x 16] as 2 x 16 MFMA
-//            16x16x32; the A operand (one latent column per lane, tokens
-//            along K) is read from the token-major tile with LDS transpose
-//            loads, and each lane's accumulator column is its own head, so
-//            rescaling needs no data movement between lanes.
+//            when a score exceeds it by more than kRaise log2 units); the
+//            weights enter the value MFMA as a bf16 value plus its bf16
+//            remainder, the running sum takes them in fp32.
+//   Output:  O^T[256 x 32] += C_tile^T[256 x 32] . P^T[32 x 32] per value
+//            wave, 8 column tiles x 2 token halves x 2 (value, remainder);
+//            the A operand (one latent column per lane, tokens along K) is
+//            read from the token-major tile with LDS transpose loads, and
+//            each lane's accumulator column is its own head, so rescaling
+//            needs no data movement between lanes.
+//   Pipeline: step t computes the scores and weights of tile t and the value
+//   product of tile t - 1, in two phases separated by barriers: (A) partial
+//   scores of tile t, first value column tiles of tile t - 1, staging of tile
+//   t + 1; (B) softmax of tile t, the remaining value column tiles.
 //   The partials (m, l, unnormalised O) go to the same workspace layout as
 //   the paged decode and are merged by the same log-sum-exp kernel.
+#include <type_traits>
+
 #include "kvd_device.h"
 #include "kvd_internal.h"
 
@@ -51,26 +63,56 @@ constexpr int kW = kDc + kDr;             // cached row width
 constexpr int kRowBytes = kW * 2;         // 1152
 constexpr int kTile = 32;                 // tokens per tile
 constexpr int kChunks = kRowBytes / 16;   // 72 16-byte chunks per row
-constexpr int kLdsRow = kRowBytes + 32;   // padded LDS row (bank spread)
+// Padded LDS row: a stride of 16 mod 256 bytes puts the 16-byte pieces of 16
+// consecutive rows in distinct bank groups.
+constexpr int kLdsRow = kRowBytes + 16;
 constexpr int kTileBytes = kTile * kLdsRow;
 constexpr int kStages = 3;                // LDS tile buffers
-constexpr int kThreads = 512;             // 8 waves: 4 head blocks x 2 halves
-constexpr int kHeadsPerWave = 16;
-constexpr int kHeadBlocks = 4;
-constexpr int kHeadsPerGroup = kHeadBlocks * kHeadsPerWave;  // 64
-constexpr int kKSteps = kW / 32 / 2;      // 9 MFMA K-steps per wave (half of 576)
-constexpr int kKBatch = 3;                // K-steps whose LDS reads are in flight together
-constexpr int kNTiles = kDc / 2 / 16;     // 16 output tiles per wave (half of 512)
+constexpr int kThreads = 512;             // 8 waves: 4 score + 4 value
+constexpr int kBlockHeads = 32;           // heads per MFMA block
+constexpr int kHeadsPerGroup = 2 * kBlockHeads;  // 64
+constexpr int kKSteps = kW / 2 / 16;      // 18 score K-steps per wave (half of 576)
+constexpr int kKBatch = 6;                // K-steps whose LDS reads are in flight together
+constexpr int kColTiles = kDc / 2 / 32;   // 8 value column tiles per wave (half of 512)
+constexpr int kColTilesA = 4;             // of which phase A runs the first kColTilesA
+constexpr int kPvAhead = 3;               // value fragments whose loads run ahead
 constexpr int kLoadWords = 18;            // 72 bytes per thread and tile
-constexpr int kXchgFloats = kWave * 8;    // one wave's partial scores
 constexpr float kRaise = 8.0f;
 
 static_assert(kKSteps % kKBatch == 0, "batched K-steps");
+static_assert(kLdsRow % 16 == 0, "16-byte aligned rows");
 // Each 16-token block (18432 bytes) is fetched by 256 threads: 4 x 16 B + 8 B.
 static_assert(kBlockTokens * kRowBytes == 256 * (4 * 16 + 8), "tile load split");
 
-__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// x, as a value the compiler must take to change at this point: addresses
+// derived from it are formed where they are used instead of being kept in
+// registers across the loop for every buffer they may point into.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Instruction-group ordering for the scheduler of the enclosing block
+// (masks of the LLVM AMDGPU scheduling-group barrier).
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+#define KVD_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Maximum of x over lanes l and l ^ 32 (the swap returns the lane's own
+// value and its partner's).
+__device__ __forceinline__ float max_over_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 struct MlaLaunchDev {
@@ -86,17 +128,25 @@ struct MlaLaunchDev {
   const uint16_t* c_new;    // fused append: [B, 576], NULL otherwise
 };
 
+struct MlaShared {
+  uint8_t tiles[kStages][kTileBytes];
+  float4 xchg[4][4][kWave];        // partial scores of each score wave
+  uint4 pw[2][2][2][kWave];        // [head block][token half][value, remainder][lane]
+  float alpha[2][kBlockHeads];     // rescale of the step, per head
+  float lsum[2][2][kWave];         // final weight sums [head block][K half][lane]
+};
+
 __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kStages][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float xchg[2][kThreads / kWave][kXchgFloats];
+  __shared__ __attribute__((aligned(16))) MlaShared sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
-  const int col = lane & 15;   // MFMA column lane: the head
-  const int kb = lane >> 4;    // MFMA K-group
-  const int hb = wave & 3;     // head block of the wave
-  const int kh = wave >> 2;    // K half of the scores, output half of the values
+  const int wave = wave_uniform(tid >> 6);
+  const bool score_wave = wave < 4;
+  const int hb = wave & 1;          // head block
+  const int hx = (wave >> 1) & 1;   // K half (score waves) or column half (value waves)
+  const int r32 = lane & 31;        // MFMA column / row lane: the head, or the token
+  const int g = lane >> 5;          // MFMA K group
 
   // Launch order: the head groups of one (sequence, partition) are 8 apart,
   // so that consecutive dispatch places them on the same XCD and the second
@@ -123,8 +173,10 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   const int ti_new = fused ? rel_new / kTile : -1;  // its tile, -1 for none
   const int r_new = rel_new % kBlockTokens;        // its row in its block
 
-  const int head0 = hg * kHeadsPerGroup + hb * kHeadsPerWave;
-  const bool active = head0 < a.num_heads;  // waves past the last head only load
+  const int head0 = hg * kHeadsPerGroup + hb * kBlockHeads;
+  const bool active = head0 < a.num_heads;  // blocks past the last head only load
+  const int head = head0 + r32;             // this lane's head
+  const bool head_ok = head < a.num_heads;
 
   // The partition's block-table entries (at most 64 blocks), one per lane,
   // read once: tile loads pick theirs with readlane, and `valid` has bit j
@@ -136,33 +188,12 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   if (lane < nblk) entry = a.block_table[static_cast<size_t>(b) * a.max_blocks_per_seq + blk0 + lane];
   const uint64_t valid = __builtin_amdgcn_ballot_w64(entry >= 0 && entry < a.num_blocks);
 
-  // Q~ as B operand: lane holds head head0 + col, K-slots
-  // 288 kh + 32 ks + 8 kb .. +7.
-  uint32_t qf[kKSteps][4];
-  {
-    const int h = active ? head0 + col : 0;
-    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(
-        a.q + (static_cast<size_t>(b) * a.num_heads + h) * kW + kh * (kW / 2));
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) load_words<4>(qf[ks], qrow + (32 * ks + 8 * kb) / 2);
-  }
-
-  // O^T accumulators: lane holds head head0 + col, latent columns
-  // 256 kh + 16 nt + 4 kb + i.
-  f32x4_t acc[kNTiles];
-#pragma unroll
-  for (int nt = 0; nt < kNTiles; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kMinusBig;  // reference max of head head0 + col (log2 units)
-  float l_lane = 0.f;       // this lane's share of the weight sum
-  const float sl2 = a.scale * kLog2e;
-
   // Tile loads: waves 0-3 fetch the tile's first 16-token block, waves 4-7
   // the second (a block is 16 x 1152 contiguous bytes), each thread 4 chunks
   // of 16 B and one of 8 B, so every load instruction uses one wave-uniform
   // buffer resource whose byte count ends at the block's last valid row.
-  const int half = wave_uniform(wave >> 2);
+  const int half = wave >> 2;
   const int lt = tid & 255;
-  uint32_t pre[2][kLoadWords];
 
   // The new row's bytes in the lanes that load them from the cache block
   // (load_tile's split of a block): at most one 16-byte chunk (c_sel) and
@@ -209,220 +240,285 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
     buffer_load_words<2>(dst + 16, r, static_cast<uint32_t>(4 * 256 * 16 + 8 * lt));
   };
   // Tile tix goes to LDS; the tile holding the new row takes it from c_new.
+  uint32_t st_off[5];  // LDS byte offsets of this thread's pieces of a tile
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int qi = lt + 256 * c;
+    st_off[c] = (half * kBlockTokens + qi / kChunks) * kLdsRow + (qi % kChunks) * 16;
+  }
+  {
+    const int o = 4 * 256 * 16 + 8 * lt;
+    st_off[4] = (half * kBlockTokens + o / kRowBytes) * kLdsRow + o % kRowBytes;
+  }
   auto store_tile = [&](const uint32_t (&src)[kLoadWords], uint8_t* tile, int tix)
       __attribute__((always_inline)) {
     const bool sub = tix == ti_new;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int qi = lt + 256 * c;
-      const int row = half * kBlockTokens + qi / kChunks, ch = qi % kChunks;
       uint4 v = make_uint4(src[4 * c], src[4 * c + 1], src[4 * c + 2], src[4 * c + 3]);
       if (sub && c == c_sel) v = new16;
-      *reinterpret_cast<uint4*>(tile + row * kLdsRow + ch * 16) = v;
+      *reinterpret_cast<uint4*>(tile + opaque(st_off[c])) = v;
     }
-    const int o = 4 * 256 * 16 + 8 * lt;
-    const int row = half * kBlockTokens + o / kRowBytes;
     uint2 t = make_uint2(src[16], src[17]);
     if (sub && tail_sel) t = new8;
-    *reinterpret_cast<uint2*>(tile + row * kLdsRow + o % kRowBytes) = t;
+    *reinterpret_cast<uint2*>(tile + opaque(st_off[4])) = t;
   };
 
-  // Valid rows of each 16-token half of tile ti (0 for a table entry outside
-  // the pool, whose rows were read as zeros and must not get weight).
-  auto half_valid = [&](int ti, int hv) __attribute__((always_inline)) {
-    const int j = 2 * ti + hv;
-    const bool ok = j < nblk && ((valid >> j) & 1);
-    return ok ? min(kBlockTokens, t_end - t_begin - j * kBlockTokens) : 0;
-  };
-
-  // Partial scores over this wave's K half: S^T lane gets head head0 + col,
-  // tokens 16 mt + 4 kb + i.  Two accumulator chains per token half.
-  auto partial_scores = [&](const uint8_t* tile, float (&part)[2][4]) __attribute__((always_inline)) {
-    f32x4_t s[2][2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      s[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    // LDS reads are issued in batches of kKBatch K-steps ahead of their MFMAs.
-    const uint8_t* arow = tile + col * kLdsRow + 16 * kb + kh * kRowBytes / 2;
-#pragma unroll
-    for (int ks0 = 0; ks0 < kKSteps; ks0 += kKBatch) {
-      uint4 av[kKBatch][2];
-#pragma unroll
-      for (int k = 0; k < kKBatch; ++k)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          av[k][mt] = *reinterpret_cast<const uint4*>(arow + 16 * mt * kLdsRow + 64 * (ks0 + k));
-#pragma unroll
-      for (int k = 0; k < kKBatch; ++k) {
-        const int ks = ks0 + k;
-        const bf16x8_t bq = as_bf16x8(qf[ks][0], qf[ks][1], qf[ks][2], qf[ks][3]);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          s[mt][ks & 1] = mfma16(as_bf16x8(av[k][mt].x, av[k][mt].y, av[k][mt].z, av[k][mt].w),
-                                 bq, s[mt][ks & 1]);
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[mt][i] = s[mt][0][i] + s[mt][1][i];
-  };
-
-  auto softmax_values = [&](int ti, const uint8_t* tile, const float (&full)[2][4])
-      __attribute__((always_inline)) {
-    const int nv0 = half_valid(ti, 0), nv1 = half_valid(ti, 1);
-    float z[2][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = 4 * kb + i < (mt ? nv1 : nv0);
-        z[mt][i] = ok ? full[mt][i] * sl2 : -INFINITY;
-        mx = fmaxf(mx, z[mt][i]);
-      }
-    mx = row_max4(mx);
-    const bool up = mx > m_run + kRaise;
-    if (__builtin_amdgcn_ballot_w64(up)) {
-      const float mn = up ? mx : m_run;
-      const float alpha = exp2_fast(m_run - mn);  // this lane's head
-      l_lane *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < kNTiles; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nt][i] *= alpha;
-      m_run = mn;
-    }
-    // Weights as the B operand: K-slot j < 4 is token 4 kb + j, j >= 4 is
-    // token 16 + 4 kb + (j - 4); a bf16 high part and its bf16 remainder
-    // (about 16 bits of weight: 8-bit weights move outputs that cancel over a
-    // few positions by ~1e-3); the sum takes the fp32 weights.
-    uint32_t pw[4], pr[4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const float p0 = exp2_fast(z[mt][2 * h2] - m_run);
-        const float p1 = exp2_fast(z[mt][2 * h2 + 1] - m_run);
-        l_lane += p0 + p1;
-        const uint32_t w = pack_bf16x2(p0, p1);
-        pw[2 * mt + h2] = w;
-        pr[2 * mt + h2] = pack_bf16x2(p0 - bf16_lo(w), p1 - bf16_hi(w));
-      }
-    }
-    const bf16x8_t pb = as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
-    const bf16x8_t prb = as_bf16x8(pr[0], pr[1], pr[2], pr[3]);
-    // Values as the A operand: lane (col, kb) of the transpose load supplies
-    // row T + col / 4 and latent columns 16 nt + 4 (col % 4) .. + 3, which
-    // leaves the lane with tokens 4 kb .. +3 (and 16 + 4 kb .. +3) of latent
-    // column 16 nt + col.
-    const uint8_t* vrow0 =
-        tile + (4 * kb + (col >> 2)) * kLdsRow + 8 * (col & 3) + kh * (kDc / 2) * 2;
-    const uint8_t* vrow1 = vrow0 + 16 * kLdsRow;
-#pragma unroll
-    for (int nt = 0; nt < kNTiles; ++nt) {
-      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(vrow0 + 32 * nt));
-      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(vrow1 + 32 * nt));
-      // Whole-vector casts: K-slots 0-3 from v0, 4-7 from v1.
-      const uint2 w0 = __builtin_bit_cast(uint2, v0);
-      const uint2 w1 = __builtin_bit_cast(uint2, v1);
-      const bf16x8_t va = as_bf16x8(w0.x, w0.y, w1.x, w1.y);
-      acc[nt] = mfma16(va, pb, acc[nt]);
-      acc[nt] = mfma16(va, prb, acc[nt]);
-    }
-  };
-
-  // Pipeline: three LDS buffers and two register slots.  Step ti computes
-  // the softmax and the value product of tile ti (buffer ti % 3) and the
-  // partial scores of tile ti + 1 (buffer (ti + 1) % 3), which are issued
-  // first so that their MFMAs overlap the softmax; tile ti + 2 moves from
-  // register slot ti % 2 into buffer (ti + 2) % 3 and slot ti % 2 starts
-  // loading tile ti + 4.  The step's one barrier at its end publishes the
-  // partial scores of tile ti + 1 (exchange buffer (ti + 1) % 2) and tile
-  // ti + 2; before it every wave has finished step ti - 1, which makes
-  // buffer (ti + 2) % 3 free.  Loads past the last tile get a zero-length
-  // resource (no memory traffic) and tiles past the last are masked out.
-  // Steps run in pairs, even step on slot 0 and odd step on slot 1, so the
-  // order of the loads in flight is the same on every pass and each store
-  // waits only for its own slot.
-  auto publish = [&](int ti, const float (&part)[2][4]) __attribute__((always_inline)) {
-    float4* xo = reinterpret_cast<float4*>(&xchg[ti & 1][wave][lane * 8]);
-    xo[0] = make_float4(part[0][0], part[0][1], part[0][2], part[0][3]);
-    xo[1] = make_float4(part[1][0], part[1][1], part[1][2], part[1][3]);
-  };
-  int cur = 0;  // ti % 3
-  float part[2][4] = {};  // this wave's partial scores of tile ti
-  auto step = [&](int ti, uint32_t (&slot)[kLoadWords]) __attribute__((always_inline)) {
-    const int nx = cur == 2 ? 0 : cur + 1;   // (ti + 1) % 3
-    const int nxt = cur == 0 ? 2 : cur - 1;  // (ti + 2) % 3
-    if (active) {
-      const float4* xp = reinterpret_cast<const float4*>(&xchg[ti & 1][wave ^ 4][lane * 8]);
-      const float4 o0 = xp[0], o1 = xp[1];
-      float next[2][4];
-      partial_scores(tiles[nx], next);
-      const float oth[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
-      // Both waves of the pair form the same sum (K half 0 first), so they
-      // take identical softmax decisions.
-      float full[2][4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          full[mt][i] = kh == 0 ? part[mt][i] + oth[mt][i] : oth[mt][i] + part[mt][i];
-      softmax_values(ti, tiles[cur], full);
-      publish(ti + 1, next);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[mt][i] = next[mt][i];
-    }
-    store_tile(slot, tiles[nxt], ti + 2);
-    load_tile(ti + 4, slot);
-    __syncthreads();
-    cur = nx;
-  };
-
+  // Register slots of the staging: step t stores tile t + 1 from slot
+  // (t + 1) % 2 into buffer (t + 1) % 3 and starts loading tile t + 3 into
+  // that slot.  Loads past the last tile get a zero-length resource (no
+  // memory traffic).  Steps run in pairs (even step on slot 1, odd on slot
+  // 0), so the order of the loads in flight is the same on every pass and
+  // each store waits only for its own slot.
+  uint32_t pre[2][kLoadWords];
   load_tile(0, pre[0]);
   load_tile(1, pre[1]);
-  store_tile(pre[0], tiles[0], 0);
-  store_tile(pre[1], tiles[1], 1);
-  load_tile(2, pre[0]);
-  load_tile(3, pre[1]);
-  __syncthreads();
-  if (active) {
-    partial_scores(tiles[0], part);
-    publish(0, part);
-  }
-  __syncthreads();
-  for (int ti = 0; ti < ntiles; ti += 2) {
-    step(ti, pre[0]);
-    step(ti + 1, pre[1]);
-  }
+  // Tile 0 into LDS (inside each branch, after the score waves have requested
+  // their query rows, so that both loads are in flight together).
+  auto first_tile = [&]() __attribute__((always_inline)) {
+    store_tile(pre[0], sh.tiles[0], 0);
+    load_tile(2, pre[0]);
+    __syncthreads();
+  };
 
-  if (!active) return;
-  const float lsum = row_sum4(l_lane);
+  const int nsteps = ntiles + 1;  // the value product trails the scores by one tile
+  auto stage = [&](int t, uint32_t (&slot)[kLoadWords]) __attribute__((always_inline)) {
+    store_tile(slot, sh.tiles[(t + 1) % kStages], t + 1);
+    load_tile(t + 3, slot);
+  };
+
   const size_t P = a.num_partitions;
-  const size_t slot = (static_cast<size_t>(b) * a.num_heads + head0 + col) * P + p;
-  if (kh == 0 && kb == 0) {
-    float2 ml;
-    ml.x = m_run;
-    ml.y = lsum;
-    reinterpret_cast<float2*>(a.ws_ml)[slot] = ml;
-  }
-  float* orow = a.ws_o + slot * kDc + kh * (kDc / 2) + 4 * kb;
+  const size_t ws_slot = (static_cast<size_t>(b) * a.num_heads + head) * P + p;
+
+  if (score_wave) {
+    // Q~ as the B operand: lane holds head `head`, K-slots
+    // 288 hx + 16 ks + 8 g .. +7.  (Marked as changed after the load, so
+    // that the compiler keeps it in registers rather than loading it again
+    // inside the loop.)
+    u32x4_t qf[kKSteps];
+    {
+      const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
+          a.q + (static_cast<size_t>(b) * a.num_heads + (head_ok ? head : 0)) * kW + hx * (kW / 2));
 #pragma unroll
-  for (int nt = 0; nt < kNTiles; ++nt)
-    *reinterpret_cast<float4*>(orow + 16 * nt) = make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = head_ok ? qrow[2 * ks + g] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    first_tile();
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
+    float m_run = kMinusBig;  // reference max of this lane's head (log2 units)
+    float l_half = 0.f;       // this lane's share of the weight sum
+    const float sl2 = a.scale * kLog2e;
+    f32x16_t s;               // this wave's partial scores of the current tile
+    const uint32_t a_off = r32 * kLdsRow + hx * (kRowBytes / 2) + 16 * g;  // A operand row piece
+
+    // Valid rows of each 16-token half of tile ti (0 for a table entry
+    // outside the pool, whose rows were read as zeros and must not get weight).
+    auto half_valid = [&](int ti, int hv) __attribute__((always_inline)) {
+      const int j = 2 * ti + hv;
+      const bool ok = j < nblk && ((valid >> j) & 1);
+      return ok ? min(kBlockTokens, t_end - t_begin - j * kBlockTokens) : 0;
+    };
+
+    auto phase_a = [&](int t) __attribute__((always_inline)) {
+      if (!active || t >= ntiles) return;
+      // A operand: lane holds token r32 of the tile, K-slots as qf.
+      const uint8_t* arow = sh.tiles[t % kStages] + opaque(a_off);
+      s = f32x16_t{};
+      uint4 av[kKSteps];
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) av[ks] = *reinterpret_cast<const uint4*>(arow + 32 * ks);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks)
+        s = mfma32(as_bf16x8(av[ks]), __builtin_bit_cast(bf16x8_t, qf[ks]), s);
+      // kKBatch reads ahead of the MFMA chain.
+      KVD_SCHED_GROUP(kSchedDsRead, kKBatch);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps - kKBatch; ++ks) {
+        KVD_SCHED_GROUP(kSchedMfma, 1);
+        KVD_SCHED_GROUP(kSchedDsRead, 1);
+      }
+      KVD_SCHED_GROUP(kSchedMfma, kKBatch);
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        sh.xchg[wave][qd][lane] = make_float4(s[4 * qd], s[4 * qd + 1], s[4 * qd + 2], s[4 * qd + 3]);
+    };
+
+    auto phase_b = [&](int t) __attribute__((always_inline)) {
+      if (!active || t >= ntiles) return;
+      // Both waves of the block form the same sum (K half 0 first), so they
+      // take identical softmax decisions.
+      float z[16];
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const float4 o = sh.xchg[wave ^ 2][qd][lane];
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[4 * qd + i] = hx == 0 ? s[4 * qd + i] + ov[i] : ov[i] + s[4 * qd + i];
+      }
+      // Register r holds token 8 (r / 4) + 4 g + r % 4 of the tile.
+      const int nv0 = half_valid(t, 0), nv1 = half_valid(t, 1);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = 8 * (r / 4) + 4 * g + (r % 4);
+        const bool ok = tok < 16 ? tok < nv0 : tok - 16 < nv1;
+        z[r] = ok ? z[r] * sl2 : -INFINITY;
+        mx = fmaxf(mx, z[r]);
+      }
+      mx = max_over_halves(mx);
+      const bool up = mx > m_run + kRaise;
+      float al = 1.f;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float mn = up ? mx : m_run;
+        al = exp2_fast(m_run - mn);
+        l_half *= al;
+        m_run = mn;
+      }
+      if (hx == 0 && g == 0) sh.alpha[hb][r32] = al;
+      // Weights of token half hx (registers 8 hx .. 8 hx + 7, the K-slots of
+      // the value product's K-step hx): a bf16 value and its bf16 remainder
+      // (about 16 bits of weight: 8-bit weights move outputs that cancel over
+      // a few positions by ~1e-3); the sum takes the fp32 weights.
+      // (A branch per half keeps the register indices static.)
+      auto weights = [&](auto half_c) __attribute__((always_inline)) {
+        constexpr int o = 8 * decltype(half_c)::value;
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2_fast(z[o + 2 * e] - m_run);
+          const float p1 = exp2_fast(z[o + 2 * e + 1] - m_run);
+          l_half += p0 + p1;
+          const uint32_t w = pack_bf16x2(p0, p1);
+          hi[e] = w;
+          lo[e] = pack_bf16x2(p0 - bf16_lo(w), p1 - bf16_hi(w));
+        }
+        sh.pw[hb][hx][0][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        sh.pw[hb][hx][1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      };
+      if (hx) weights(std::integral_constant<int, 1>{});
+      else weights(std::integral_constant<int, 0>{});
+    };
+
+    for (int t = 0; t < nsteps; t += 2) {
+      phase_a(t);
+      stage(t, pre[1]);
+      __syncthreads();
+      phase_b(t);
+      __syncthreads();
+      phase_a(t + 1);
+      stage(t + 1, pre[0]);
+      __syncthreads();
+      phase_b(t + 1);
+      __syncthreads();
+    }
+    // Weight sum of the head: both K halves, both half-waves.
+    sh.lsum[hb][hx][lane] = l_half;
+    __syncthreads();
+    if (active && hx == 0 && g == 0 && head_ok) {
+      const float l = (sh.lsum[hb][0][lane] + sh.lsum[hb][1][lane]) +
+                      (sh.lsum[hb][0][lane + 32] + sh.lsum[hb][1][lane + 32]);
+      reinterpret_cast<float2*>(a.ws_ml)[ws_slot] = make_float2(m_run, l);
+    }
+  } else {
+    // O^T accumulators: lane holds head `head`, latent columns
+    // 256 hx + 32 ct + 8 (r / 4) + 4 g + r % 4 in register r of tile ct.
+    first_tile();
+    f32x16_t acc[kColTiles];
+#pragma unroll
+    for (int ct = 0; ct < kColTiles; ++ct) acc[ct] = f32x16_t{};
+    uint4 pv[2][2];  // weights of the tile: [token half][value, remainder]
+
+    // A operand of column tile ct, token half j: lane (row r32, K group g)
+    // gets tokens 16 j + 4 g + 0..3 and 16 j + 8 + 4 g + 0..3 of latent
+    // column 256 hx + 32 ct + r32 from two transpose loads; within each
+    // 16-lane group, lane i supplies row (i / 4) of the four and columns
+    // 4 (i % 4) .. +3 of the group's sixteen.
+    const int gi = lane & 15;
+    const uint32_t v_off = (4 * g + (gi >> 2)) * kLdsRow +
+                           (hx * (kDc / 2) + 16 * ((lane >> 4) & 1) + 4 * (gi & 3)) * 2;
+    // The transpose loads run kPvAhead fragments ahead of their MFMAs.
+    auto pv_tiles = [&](const uint8_t* tile, auto ct0_c, auto ct1_c) __attribute__((always_inline)) {
+      constexpr int ct0 = decltype(ct0_c)::value, ct1 = decltype(ct1_c)::value;
+      const uint8_t* vb = tile + opaque(v_off);
+      uint2 w[ct1 - ct0][2][2];
+#pragma unroll
+      for (int ct = ct0; ct < ct1; ++ct)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            w[ct - ct0][j][hh] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t*)(vb + (16 * j + 8 * hh) * kLdsRow + 64 * ct)));
+#pragma unroll
+      for (int ct = ct0; ct < ct1; ++ct)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint2 w0 = w[ct - ct0][j][0], w1 = w[ct - ct0][j][1];
+          const bf16x8_t va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+          acc[ct] = mfma32(va, as_bf16x8(pv[j][0]), acc[ct]);
+          acc[ct] = mfma32(va, as_bf16x8(pv[j][1]), acc[ct]);
+        }
+      constexpr int frags = 2 * (ct1 - ct0);
+      KVD_SCHED_GROUP(kSchedDsRead, 2 * kPvAhead);
+#pragma unroll
+      for (int f = 0; f < frags - kPvAhead; ++f) {
+        KVD_SCHED_GROUP(kSchedMfma, 2);
+        KVD_SCHED_GROUP(kSchedDsRead, 2);
+      }
+      KVD_SCHED_GROUP(kSchedMfma, 2 * kPvAhead);
+    };
+
+    auto phase_a = [&](int t) __attribute__((always_inline)) {
+      if (!active || t < 1 || t > ntiles) return;
+      const float al = sh.alpha[hb][r32];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        pv[j][0] = sh.pw[hb][j][0][lane];
+        pv[j][1] = sh.pw[hb][j][1][lane];
+      }
+      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+#pragma unroll
+        for (int ct = 0; ct < kColTiles; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[ct][r] *= al;
+      }
+      pv_tiles(sh.tiles[(t - 1) % kStages], std::integral_constant<int, 0>{},
+               std::integral_constant<int, kColTilesA>{});
+    };
+    auto phase_b = [&](int t) __attribute__((always_inline)) {
+      if (!active || t < 1 || t > ntiles) return;
+      pv_tiles(sh.tiles[(t - 1) % kStages], std::integral_constant<int, kColTilesA>{},
+               std::integral_constant<int, kColTiles>{});
+    };
+
+    for (int t = 0; t < nsteps; t += 2) {
+      phase_a(t);
+      stage(t, pre[1]);
+      __syncthreads();
+      phase_b(t);
+      __syncthreads();
+      phase_a(t + 1);
+      stage(t + 1, pre[0]);
+      __syncthreads();
+      phase_b(t + 1);
+      __syncthreads();
+    }
+    __syncthreads();  // matches the score waves' weight-sum exchange
+    if (!active || !head_ok) return;
+    float* orow = a.ws_o + ws_slot * kDc + hx * (kDc / 2) + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < kColTiles; ++ct)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<float4*>(orow + 32 * ct + 8 * qd) =
+            make_float4(acc[ct][4 * qd], acc[ct][4 * qd + 1], acc[ct][4 * qd + 2], acc[ct][4 * qd + 3]);
+  }
 }
 
 }  // namespace
 
 bool mla_supported(int num_heads, int d_c, int d_rope) {
-  return d_c == kDc && d_rope == kDr && num_heads >= kHeadsPerWave && num_heads % kHeadsPerWave == 0;
+  return d_c == kDc && d_rope == kDr && num_heads >= 16 && num_heads % 16 == 0;
 }
 
 int mla_head_groups(int num_heads) { return (num_heads + kHeadsPerGroup - 1) / kHeadsPerGroup; }

@@ -181,8 +181,8 @@ size_t decode_attn_workspace_bytes(int batch, int num_q_heads, int num_kv_heads,
  *   q                [batch, num_q_heads, head_dim], dtype
  *   k_cache, v_cache [num_blocks, 16, num_kv_heads, head_dim], dtype
  *   head_dim         32, 64 or 128
- *   num_q_heads      a multiple of num_kv_heads; the ratio 1, 2, 4, 8 or a
- *                    multiple of 8 up to 64
+ *   num_q_heads      a multiple of num_kv_heads; the ratio 1, 2 or a
+ *                    multiple of 4 up to 64
  *   max_seq_len      host-known upper bound of seq_lens (sizes the grid)
  *   scale            score scale, normally 1/sqrt(head_dim)
  *   partition_tokens 0 for automatic, else a multiple of 16
@@ -348,8 +348,9 @@ int kvd_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes
  *   out[b][h] = sum_t softmax(z)_t c_t  (latent space, width d_c)
  * The caller chooses `scale` (the Python binding defaults to 1/sqrt(d_c/4 +
  * d_rope), the per-head width of the un-absorbed key when d_c = 4 d_h).
- * Both products run on bf16 MFMA with fp32 accumulation; softmax weights are
- * rounded to bf16 before the value product, the sum uses the same weights.
+ * Both products run on bf16 MFMA with fp32 accumulation.  Each softmax
+ * weight enters the value product as a bf16 value plus its bf16 remainder
+ * (about 16 bits of the weight); the weight sum takes the fp32 weights.
  *
  *   out      [batch, num_q_heads, d_c] bf16
  *   q        [batch, num_q_heads, d_c + d_rope] bf16
@@ -455,7 +456,15 @@ int kv_append_paged_int8(int8_t* k_cache, int8_t* v_cache, float* v_scale, const
  * attention with K[t][g][j] = k_scale[g][j] * code and V[t][g][j] =
  * v_scale[t][g] * code.  The scales are folded into the query (per channel)
  * and into the softmax weights (per token) in registers; the codes are
- * widened to bf16 exactly and the products accumulate in fp32.
+ * widened to fp16 exactly and the products accumulate in fp32.
+ * Range: the scaled query q * k_scale and the weights times the V scales
+ * (weights reach 2^8 before normalisation) are fp16 operands, so
+ *   |q[b][h][j] * k_scale[g][j]| <= 65504 and v_scale[t][g] <= 255
+ * (INT8: |V| up to ~32,000; FP8: up to ~114,000) keep the result finite;
+ * beyond them the output holds inf or NaN.  Weight-scale products below
+ * fp16's smallest normal number (6.1e-5) keep an absolute precision of
+ * 6e-8 (2^-24) instead of 11 significant bits, which matters only for V
+ * scales far below the 1e-2 .. 1e2 of typical activations.
  *   q, out     [batch, num_q_heads, head_dim] bf16 (dtype must be KVD_BF16)
  *   k_scale    16-byte aligned; v_scale 4-byte aligned
  * Other arguments (head_dim, ratios, partition_tokens, workspace), errors and

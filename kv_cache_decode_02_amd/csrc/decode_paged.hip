@@ -1230,12 +1230,33 @@ hipError_t launch_variant(const PagedLaunch& a, int hpw, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Balanced split: as many workgroups as are resident at once (4 * WPE
-// wavefronts per compute unit, in workgroups of WG waves).
+// LDS bytes per compute unit of the current device (cached per device;
+// 160 KiB on MI355X).
+size_t device_lds_per_cu() {
+  static size_t lds[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 160 * 1024;
+  if (lds[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess || n < 1)
+      n = 160 * 1024;
+    lds[dev] = static_cast<size_t>(n);
+  }
+  return lds[dev];
+}
+
+// Balanced split: as many workgroups as are resident at once: 4 * WPE
+// wavefronts per compute unit in workgroups of WG waves, or fewer when their
+// LDS (the static wave slices and the two batch prefixes) does not fit that
+// many (large batches on four-wave workgroups).
 template <class W, int WPE, int WG>
 hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
   const size_t lds = 2 * static_cast<size_t>(a.batch + 1) * sizeof(int);
-  const int groups = device_cus() * ((4 * WPE) / WG);
+  const size_t lds_wg = lds + WG * W::kLdsPerWave + 16;
+  const int by_waves = (4 * WPE) / WG;
+  const int by_lds = static_cast<int>(device_lds_per_cu() / lds_wg);
+  const int groups = device_cus() * max(1, min(by_waves, by_lds));
   hipLaunchKernelGGL((paged_balanced_kernel<W, WPE, WG>),
                      dim3(static_cast<unsigned>(groups)), dim3(64 * WG), lds, stream, a);
   return hipGetLastError();

@@ -162,6 +162,38 @@ def test_fp8_phases_equal_single_call():
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
+LARGE_V_CASES = [("gqa-r4", dict(H_q=32, H_kv=8)), ("mha", dict(H_q=8, H_kv=8))]
+
+
+@pytest.mark.parametrize("name,c", LARGE_V_CASES, ids=[n for n, _ in LARGE_V_CASES])
+def test_decode_fp8_large_v_rows(name, c):
+    # History codes over every finite magnitude and V scales times 2^15: V
+    # magnitudes up to 448 * 192 ~ 8.6e4, and weight times V scale products
+    # up to 2^8 * 192 = 49152, inside the fp16 operand range (65504) that the
+    # one-byte decode documents for them.
+    log(f"fp8 decode large V rows {name}")
+    inp = make_paged_decode_fp8(np.random.default_rng(zlib.crc32(name.encode()) + 31), 3,
+                                c["H_q"], c["H_kv"], 128, [40, 1500, 4096], full_range=True)
+    inp.vs_pool = (inp.vs_pool * np.float32(2.0 ** 15)).astype(np.float32)
+    owned = np.isin(np.arange(inp.num_blocks), inp.block_table)
+    assert np.nanmax(inp.vs_pool[owned]) > 150.0
+    dev = Fp8Dev(inp)
+    dev.append()
+    out = kvd.decode_attn_paged_fp8(dev.q, dev.kq, dev.vq, dev.ks, dev.vs, dev.table, dev.seq,
+                   inp.max_seq_len)
+    torch.cuda.synchronize()
+    kq, vq, vs = _oracle_step(inp)
+    ref = oracle.decode_attn_paged_fp8(inp.q, kq, vq, vs, inp.k_scale, inp.block_table,
+                      inp.seq_lens, "bf16")
+    assert np.max(np.abs(ref)) > 100.0
+    got = down_f64(out)
+    assert np.all(np.isfinite(got))
+    # The output is linear in V: compared in units of the factor, which is
+    # the contract for the same inputs with the unscaled V (2^15 is exact).
+    rep = assert_contract(got / 2.0 ** 15, ref / 2.0 ** 15, name)
+    log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")
+
+
 def test_fp8_full_size_sampled():
     name = "gqa_llama3_8b_fp8"
     log(f"full {name}: generating")

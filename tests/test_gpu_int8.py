@@ -148,6 +148,37 @@ def test_int8_phases_equal_single_call():
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
+LARGE_V_CASES = [("gqa-r4", dict(H_q=32, H_kv=8)), ("mha", dict(H_q=8, H_kv=8))]
+
+
+@pytest.mark.parametrize("name,c", LARGE_V_CASES, ids=[n for n, _ in LARGE_V_CASES])
+def test_decode_int8_large_v_rows(name, c):
+    # History V scales times 2^13: V magnitudes up to ~2.4e4, and weight times
+    # V scale products up to 2^8 * 192 = 49152, inside the fp16 operand range
+    # (65504) that the one-byte decode documents for them.
+    log(f"int8 decode large V rows {name}")
+    inp = make_paged_decode_int8(np.random.default_rng(zlib.crc32(name.encode()) + 31), 3,
+                                 c["H_q"], c["H_kv"], 128, [40, 1500, 4096])
+    inp.vs_pool = (inp.vs_pool * np.float32(2.0 ** 13)).astype(np.float32)
+    owned = np.isin(np.arange(inp.num_blocks), inp.block_table)
+    assert np.nanmax(inp.vs_pool[owned]) > 150.0
+    dev = Int8Dev(inp)
+    dev.append()
+    out = kvd.decode_attn_paged_int8(dev.q, dev.kq, dev.vq, dev.ks, dev.vs, dev.table, dev.seq,
+                   inp.max_seq_len)
+    torch.cuda.synchronize()
+    kq, vq, vs = _oracle_step(inp)
+    ref = oracle.decode_attn_paged_int8(inp.q, kq, vq, vs, inp.k_scale, inp.block_table,
+                      inp.seq_lens, "bf16")
+    assert np.max(np.abs(ref)) > 100.0
+    got = down_f64(out)
+    assert np.all(np.isfinite(got))
+    # The output is linear in V: compared in units of the factor, which is
+    # the contract for the same inputs with the unscaled V (2^13 is exact).
+    rep = assert_contract(got / 2.0 ** 13, ref / 2.0 ** 13, name)
+    log(f"  max_err {rep['max_err']:.3e} scaled {rep['scaled']:.3e}")
+
+
 def test_int8_full_size_sampled():
     name = "gqa_llama3_8b_int8"
     log(f"full {name}: generating")

@@ -23,7 +23,7 @@ constexpr int kMaxPartition = 1024;   // 64 blocks: one block id per lane
 constexpr long long kTargetWaves = 12288;
 constexpr long long kMlaTargetGroups = 256;  // one workgroup per compute unit
 constexpr int kLatentWidth = 512;
-constexpr int kMaxBalancedBatch = 8191;  // two prefixes of the batch in LDS (64 KiB)
+constexpr int kMaxBalancedBatch = 8191;  // two prefixes and the lengths in LDS (96 KiB)
 constexpr int kMaxTableBlocks = 1 << 26;  // keeps max_blocks_per_seq * 16 in int
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }

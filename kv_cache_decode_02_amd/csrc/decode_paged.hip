@@ -558,10 +558,9 @@ __device__ __forceinline__ int first_visible(const PagedLaunch& a, int len) {
   return a.window > 0 ? max(0, len - a.window) : 0;
 }
 
-// Blocks of sequence b that hold visible positions (lengths clamped to
-// max_seq_len), from block first_visible / 16 on.
-__device__ __forceinline__ int seq_blocks(const PagedLaunch& a, int b) {
-  const int len = min(a.seq_lens[b], a.max_seq_len);
+// Blocks of a sequence of len positions (clamped to max_seq_len) that hold
+// visible positions, from block first_visible / 16 on.
+__device__ __forceinline__ int visible_blocks(const PagedLaunch& a, int len) {
   if (len <= 0) return 0;
   return (len + kBlockTokens - 1) / kBlockTokens - first_visible(a, len) / kBlockTokens;
 }
@@ -575,10 +574,13 @@ struct ValuWorker {
   static constexpr int kLdsPerWave = 0;
   static constexpr long long kEvenXcdShare = 1120;
   static __device__ __forceinline__ int heads_per_wave(int /*ratio*/) { return HPW; }
+  struct Pre {};  // (this flavour issues its first requests inside attend)
+  static __device__ __forceinline__ void prefetch(const PagedLaunch&, int, int, int, int, int,
+                                                  Pre&) {}
   static __device__ __forceinline__ void unit(const PagedLaunch& a, int lane, unsigned char* /*lds*/,
                                               int b, int g, int h0, int j_begin, int j_end,
                                               int t_start, int t_end, bool fused, bool write_new,
-                                              size_t slot0, size_t P) {
+                                              size_t slot0, size_t P, const Pre&, int) {
     HeadState<HPW, D / 8> st;
     attend<KT, D, HPW, NBUF>(a, lane, b, g, h0, j_begin, j_end, t_start, t_end, st, fused,
                              write_new);
@@ -880,39 +882,78 @@ struct MfmaWorker {
     write(a, lane, slot0, P, heads_per_wave(ratio), st);
   }
 
-  // Queries of heads h0 .. h0 + nheads - 1 as the B operand (head lane % 16,
-  // zero past the wave's heads).  bf16 caches: the bf16 queries.  One-byte
-  // caches: q times K/V head g's per-channel K scales, rounded to fp16
-  // (q . (s * code) = (q * s) . code); INT8 also returns the score offset
-  // -kI8Bias * (sum of the head's scaled query), from the same fp16 values.
-  static __device__ __forceinline__ float load_q(const PagedLaunch& a, int lane, int b, int h0,
-                                                 int g, int nheads, uint32_t (&q)[D / 32][4]) {
+  // The first requests of a unit, issued before anything waits on memory, so
+  // that they share one round trip (and, in the kernels, the one that reads
+  // the sequence length): the block ids of blocks j_pre .. j_pre + 63 of
+  // sequence b (one per lane; lanes past the table row read 0) and the query
+  // rows of heads h0 .. h0 + nheads - 1 in the B operand's layout (head
+  // lane % 16, zeros past the wave's heads), with the K/V head's per-channel
+  // K scales for one-byte caches.  The ids are requested first: waiting for
+  // them does not wait for the queries.
+  // Block id of block j + lane of sequence b's table row (0 past the row).
+  static __device__ __forceinline__ int table_ids(const PagedLaunch& a, int b, int j, int lane) {
+    const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
+    const int left = wave_uniform(min(max(0, a.max_blocks_per_seq - j), kWave));
+    const BufRsrc rt = make_rsrc(trow + min(j, a.max_blocks_per_seq), left * 4);
+    return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * lane, 0, 0));
+  }
+  struct Pre {
+    int ids;                  // block id of block j_pre + lane
+    uint32_t qw[S::KS][4];    // query words (bf16)
+    float4 ks[S::KS][2];      // one-byte caches: K scales of those dimensions
+  };
+  static __device__ __forceinline__ void prefetch(const PagedLaunch& a, int lane, int b, int g,
+                                                  int h0, int j_pre, Pre& pr) {
+    const int ratio = a.num_q_heads / a.num_kv_heads;
+    const int nheads = heads_per_wave(ratio);
     const int G = lane >> 4, i = lane & 15;
-    const bool live = i < nheads;
-    const uint32_t* qrow = static_cast<const uint32_t*>(a.q) +
-                           (static_cast<size_t>(b) * a.num_q_heads + h0 + (live ? i : 0)) * (D / 2);
+    pr.ids = table_ids(a, b, j_pre, lane);
+    const BufRsrc rq = make_rsrc(static_cast<const uint16_t*>(a.q) +
+                                     (static_cast<size_t>(b) * a.num_q_heads + h0) * D,
+                                 nheads * D * 2);
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s)
+      buffer_load_words<4>(pr.qw[s], rq, static_cast<uint32_t>((i * D + S::kdim(s, G)) * 2));
+    if constexpr (KT != kBF16) {
+#pragma unroll
+      for (int s = 0; s < S::KS; ++s) {
+        const float* ks = a.k_scale + static_cast<size_t>(g) * D + S::kdim(s, G);
+        pr.ks[s][0] = *reinterpret_cast<const float4*>(ks);
+        pr.ks[s][1] = *reinterpret_cast<const float4*>(ks + 4);
+      }
+    }
+  }
+
+  // The prefetched queries as the B operand.  bf16 caches: the bf16 queries.
+  // One-byte caches: q times K/V head g's per-channel K scales, rounded to
+  // fp16 (q . (s * code) = (q * s) . code); INT8 also returns the score offset
+  // -kI8Bias * (sum of the head's scaled query), from the same fp16 values.
+  // The empty asm statements pin the arithmetic here: hoisted above the
+  // first block loads, it would make them wait for the queries.
+  static __device__ __forceinline__ float make_q(Pre pr, uint32_t (&q)[D / 32][4]) {
     float qs = 0.f;
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
-      const int d0 = S::kdim(s, G);
-      uint32_t w[4];
-      load_words<4>(w, qrow + d0 / 2);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(pr.qw[s][k]));
+      if constexpr (KT != kBF16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          asm volatile("" : "+v"(pr.ks[s][h].x), "+v"(pr.ks[s][h].y), "+v"(pr.ks[s][h].z),
+                       "+v"(pr.ks[s][h].w));
+      }
       if constexpr (KT == kBF16) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) q[s][k] = live ? w[k] : 0u;
+        for (int k = 0; k < 4; ++k) q[s][k] = pr.qw[s][k];
       } else {
-        const float* ks = a.k_scale + static_cast<size_t>(g) * D + d0;
-        const float4 s0 = *reinterpret_cast<const float4*>(ks);
-        const float4 s1 = *reinterpret_cast<const float4*>(ks + 4);
+        const uint32_t* w = pr.qw[s];
+        const float4 s0 = pr.ks[s][0], s1 = pr.ks[s][1];
         q[s][0] = pack_f16x2(bf16_lo(w[0]) * s0.x, bf16_hi(w[0]) * s0.y);
         q[s][1] = pack_f16x2(bf16_lo(w[1]) * s0.z, bf16_hi(w[1]) * s0.w);
         q[s][2] = pack_f16x2(bf16_lo(w[2]) * s1.x, bf16_hi(w[2]) * s1.y);
         q[s][3] = pack_f16x2(bf16_lo(w[3]) * s1.z, bf16_hi(w[3]) * s1.w);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (!live) q[s][k] = 0u;
-          qs = dot2_f16(q[s][k], kF16OnePair, qs);
-        }
+        for (int k = 0; k < 4; ++k) qs = dot2_f16(q[s][k], kF16OnePair, qs);
       }
     }
     return KT == kI8 ? -kI8Bias * row_sum4(qs) : 0.f;
@@ -923,16 +964,16 @@ struct MfmaWorker {
   // `fused` (bf16 caches) the range ends at position t_end - 1, which is
   // taken from k_new / v_new as a one-token block after the others, and with
   // `write_new` the wave also stores head g's part of those rows into their
-  // cache slot.
+  // cache slot.  `pr` holds this unit's prefetch for blocks j_pre .. +63.
   static __device__ __forceinline__ void unit(const PagedLaunch& a, int lane, unsigned char* lds,
                                               int b, int g, int h0, int j_begin, int j_end,
                                               int t_start, int t_end, bool fused, bool write_new,
-                                              size_t slot0, size_t P) {
+                                              size_t slot0, size_t P, const Pre& pr, int j_pre) {
     const int ratio = a.num_q_heads / a.num_kv_heads;
     const int nheads = heads_per_wave(ratio);
     const int G = lane >> 4, i = lane & 15;
     uint32_t q[S::KS][4];
-    const float qb = load_q(a, lane, b, h0, g, nheads, q);
+    float qb = 0.f;
     MState<D> st;
     reset(st);
     const int t_last = t_end - 1;
@@ -940,22 +981,34 @@ struct MfmaWorker {
     const float sl2 = a.scale * kLog2e;
     const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
     MFrag<KT, D> buf[NBUF];
+    if (j_begin >= j_end) qb = make_q(pr, q);  // (no cached block: the fused row only)
 
+    // The first chunk's ids are the prefetched ones (callers start the
+    // prefetch at or before j_begin and no more than 64 blocks before the
+    // chunk's end); each chunk requests the next one's ids (lane k: block
+    // c0 + 64 + k) before it waits on anything, with no branch, so that no
+    // wait has to cover a load that only some paths issue.
+    int my_id = pr.ids, off = j_begin - j_pre;
     for (int c0 = j_begin; c0 < j_end; c0 += kMaxPartitionBlocks) {
       const int nblk = min(kMaxPartitionBlocks, j_end - c0);
-      const int my_id = lane < nblk ? trow[c0 + lane] : -1;
+      const int next_id = table_ids(a, b, c0 + kMaxPartitionBlocks, lane);
       auto block_of = [&](int jj, int& nvalid) __attribute__((always_inline)) {
-        const int blk = __builtin_amdgcn_readlane(my_id, jj & (kWave - 1));
+        const int blk = __builtin_amdgcn_readlane(my_id, (off + jj) & (kWave - 1));
         const bool ok = jj < nblk && blk >= 0 && blk < a.num_blocks;
         nvalid = ok ? min(kBlockTokens, t_end - (c0 + jj) * kBlockTokens) : 0;
         return blk;
       };
+      // (In buffer order: the scheduler would otherwise be free to issue the
+      // first block's loads last, and the first wait would cover them all.)
 #pragma unroll
       for (int s0 = 0; s0 < NBUF; ++s0) {
         int nv;
         const int blk = block_of(s0, nv);
         mfma_block_rows<KT, D>(buf[s0], a, lane, g, blk, nv);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // The queries are formed after the first block loads are on their way.
+      if (c0 == j_begin) qb = make_q(pr, q);
       for (int base = 0; base < nblk; base += NBUF) {
 #pragma unroll
         for (int s0 = 0; s0 < NBUF; ++s0) {
@@ -972,6 +1025,8 @@ struct MfmaWorker {
         }
       }
       if constexpr (KT == kI8) mfma_unbias(st);
+      my_id = next_id;
+      off = 0;
     }
     if constexpr (KT == kBF16) {
       if (fused) {
@@ -1030,13 +1085,21 @@ void paged_partials_kernel(PagedLaunch a) {
   const int p = u % a.num_partitions;
   const int b = u / a.num_partitions;
 
+  // The sequence length, the partition's block ids and the queries are
+  // requested together (the length first), before anything waits.
   int len = a.seq_lens[b];
-  len = min(len, a.max_seq_len);
   const int p_begin = p * a.partition_tokens;
+  const int h0 = g * ratio + hc * hpw;
+  const int j_pre = p_begin / kBlockTokens;
+  typename W::Pre pr;
+  W::prefetch(a, lane, b, g, h0, j_pre, pr);
+  // (Keeps the requests above the early exit below: sunk past it, they
+  // would wait for the length.)
+  asm volatile("" ::: "memory");
+  len = min(len, a.max_seq_len);
   if (len <= p_begin) return;
   const int t_end = min(len, p_begin + a.partition_tokens);
   const int t_begin = max(p_begin, first_visible(a, len));
-  const int h0 = g * ratio + hc * hpw;
   const size_t P = a.num_partitions;
   const size_t slot0 = (static_cast<size_t>(b) * a.num_q_heads + h0) * P + p;
   if (t_begin >= t_end) {
@@ -1048,7 +1111,8 @@ void paged_partials_kernel(PagedLaunch a) {
   const int nblk = (t_end + kBlockTokens - 1) / kBlockTokens - j0;
 
   const bool fused = a.k_new != nullptr && t_end == len;
-  W::unit(a, lane, lds, b, g, h0, j0, j0 + nblk, t_begin, t_end, fused, hc == 0, slot0, P);
+  W::unit(a, lane, lds, b, g, h0, j0, j0 + nblk, t_begin, t_end, fused, hc == 0, slot0, P, pr,
+          j_pre);
 }
 
 // Balanced split (automatic mode).  The work list is every (sequence b,
@@ -1071,10 +1135,12 @@ template <class W, int WPE, int WG>
 __global__ __launch_bounds__(64 * WG) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void paged_balanced_kernel(PagedLaunch a) {
   __shared__ __attribute__((aligned(16))) unsigned char wave_lds[WG * W::kLdsPerWave + 16];
-  // [batch + 1] blocks of the sequences before b, then [batch + 1] count of
-  // the non-empty sequences before b.
+  // [batch + 1] blocks of the sequences before b, [batch + 1] count of the
+  // non-empty sequences before b, then [batch] lengths clamped to
+  // max_seq_len.
   extern __shared__ int blk_prefix[];
   int* const seq_prefix = blk_prefix + a.batch + 1;
+  int* const len_of = seq_prefix + a.batch + 1;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x >> 6);
   unsigned char* lds = wave_lds + wave * W::kLdsPerWave;
@@ -1087,8 +1153,10 @@ void paged_balanced_kernel(PagedLaunch a) {
   if (wave == 0) {
     int run = 0, run_seq = 0;
     for (int c = 0; c < a.batch; c += kWave) {
-      int x = c + lane < a.batch ? seq_blocks(a, c + lane) : 0;
+      const int len = c + lane < a.batch ? min(a.seq_lens[c + lane], a.max_seq_len) : 0;
+      int x = visible_blocks(a, len);
       int y = x > 0 ? 1 : 0;
+      if (c + lane < a.batch) len_of[c + lane] = len;
 #pragma unroll
       for (int sh = 1; sh < kWave; sh <<= 1) {
         const int xs = __shfl_up(x, sh, kWave);
@@ -1185,15 +1253,19 @@ void paged_balanced_kernel(PagedLaunch a) {
     if (u < units) {
       const int g = u / hchunks, hc = u % hchunks;
       const int h0 = g * ratio + hc * hpw;
-      const int t_end = wave_uniform(min(a.seq_lens[b], a.max_seq_len));
+      const int t_end = wave_uniform(len_of[b]);
       const int t_start = first_visible(a, t_end);
       const int js = t_start / kBlockTokens;  // the sequence's first visible block
+      // The block ids from the segment's first block and the queries are
+      // requested together, before anything waits on memory.
+      typename W::Pre pr;
+      W::prefetch(a, lane, b, g, h0, js + j0, pr);
       const bool fused = a.k_new != nullptr && seg_end == seg_begin + nb;
       const int first = owner(vpos(b, ug, nb, 0));
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
       W::unit(a, lane, lds, b, g, h0, js + j0, js + j0 + (seg_end - item), t_start, t_end, fused,
-              hc == 0, row0 * P + piece, P);
+              hc == 0, row0 * P + piece, P, pr, js + j0);
       if (piece == 0 && lane < hpw)
         a.counts[row0 + lane] = owner(vpos(b, ug, nb, nb - 1)) - first + 1;
     }
@@ -1252,7 +1324,7 @@ size_t device_lds_per_cu() {
 // many (large batches on four-wave workgroups).
 template <class W, int WPE, int WG>
 hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
-  const size_t lds = 2 * static_cast<size_t>(a.batch + 1) * sizeof(int);
+  const size_t lds = (3 * static_cast<size_t>(a.batch) + 2) * sizeof(int);
   const size_t lds_wg = lds + WG * W::kLdsPerWave + 16;
   const int by_waves = (4 * WPE) / WG;
   const int by_lds = static_cast<int>(device_lds_per_cu() / lds_wg);

@@ -13,40 +13,37 @@
 // Work decomposition:
 //   workgroup = (sequence b, partition p, group of 64 query heads), 8 waves,
 //   two blocks of 32 heads.  The waves specialise:
-//     score waves 0-3   (head block w & 1, K half w >> 1): partial scores
-//                       over their half of the 576-wide rows, Q~ held in
-//                       registers; the two halves are added through LDS and
-//                       both waves of a block take the same softmax
-//                       decisions; each writes the weights of one 16-token
-//                       half of the tile to LDS;
-//     value waves 4-7   (head block w & 1, column half (w - 4) >> 1): the
-//                       unnormalised output of 32 heads x 256 latent columns
-//                       in registers, fed by those weights.
-//   With the usual placement of wave w on SIMD w % 4 every SIMD holds one
-//   score wave and one value wave, so the softmax arithmetic of the one
-//   overlaps the matrix products of the other.  Every LDS fragment of the
-//   tile feeds the MFMAs of 32 heads.
+//     score waves 0-1   (head block w): the full 576-wide scores of 32 heads,
+//                       Q~ held in registers, then the online softmax; each
+//                       writes the weights of its block to LDS;
+//     value waves 2-7   (a range of 32-column tiles of the latent, both head
+//                       blocks): the unnormalised output of 64 heads x their
+//                       columns in registers, fed by those weights.  Waves
+//                       4 and 5 share a SIMD with the score waves (wave w
+//                       runs beside wave w + 4) and take two column tiles,
+//                       the others three, so every SIMD issues about the
+//                       same number of MFMAs per tile.
 //   Tokens come in tiles of 32 (two 16-token blocks), loaded once per
 //   workgroup through the block table (rows past the sequence end read as
-//   zeros), stored token-major in LDS and shared by all 8 waves.  The two head
-//   groups of one (sequence, partition) are launched 8 workgroups apart, so
-//   they run on the same XCD and the second reads the tiles from L2.
-//   Scores:  S^T[token][head] = C_tile[32 x 288] . Q~^T[288 x 32] per score
-//            wave, 18 MFMAs; every lane ends with one head and 16 tokens.
+//   zeros) by the value waves, stored token-major in LDS and read by all 8
+//   waves.  The two head groups of one (sequence, partition) are launched 8
+//   workgroups apart, so they run on the same XCD and the second reads the
+//   tiles from L2.
+//   Scores:  S^T[token][head] = C_tile[32 x 576] . Q~^T[576 x 32] per score
+//            wave, 36 MFMAs; every lane ends with one head and 16 tokens.
 //   Softmax: online per head with a lazily raised reference max (raised only
 //            when a score exceeds it by more than kRaise log2 units); the
 //            weights enter the value MFMA as a bf16 value plus its bf16
 //            remainder, the running sum takes them in fp32.
-//   Output:  O^T[256 x 32] += C_tile^T[256 x 32] . P^T[32 x 32] per value
-//            wave, 8 column tiles x 2 token halves x 2 (value, remainder);
-//            the A operand (one latent column per lane, tokens along K) is
-//            read from the token-major tile with LDS transpose loads, and
-//            each lane's accumulator column is its own head, so rescaling
-//            needs no data movement between lanes.
+//   Output:  O^T[32 x 32] += C_tile^T[32 x 32] . P^T[32 x 32] per column
+//            tile, token half and head block, twice (value, remainder); the
+//            A operand (one latent column per lane, tokens along K) is read
+//            from the token-major tile with LDS transpose loads and feeds the
+//            MFMAs of both head blocks, and each lane's accumulator column is
+//            its own head, so rescaling needs no data movement between lanes.
 //   Pipeline: step t computes the scores and weights of tile t and the value
-//   product of tile t - 1, in two phases separated by barriers: (A) partial
-//   scores of tile t, first value column tiles of tile t - 1, staging of tile
-//   t + 1; (B) softmax of tile t, the remaining value column tiles.
+//   product of tile t - 1, and stages tile t + 1, with one barrier per step;
+//   the weights and rescale factors alternate between two LDS buffers.
 //   The partials (m, l, unnormalised O) go to the same workspace layout as
 //   the paged decode and are merged by the same log-sum-exp kernel.
 #include <type_traits>
@@ -68,21 +65,28 @@ constexpr int kChunks = kRowBytes / 16;   // 72 16-byte chunks per row
 constexpr int kLdsRow = kRowBytes + 16;
 constexpr int kTileBytes = kTile * kLdsRow;
 constexpr int kStages = 3;                // LDS tile buffers
-constexpr int kThreads = 512;             // 8 waves: 4 score + 4 value
+constexpr int kThreads = 512;             // 8 waves: 2 score + 6 value
 constexpr int kBlockHeads = 32;           // heads per MFMA block
 constexpr int kHeadsPerGroup = 2 * kBlockHeads;  // 64
-constexpr int kKSteps = kW / 2 / 16;      // 18 score K-steps per wave (half of 576)
+constexpr int kKSteps = kW / 16;          // 36 score K-steps (all of 576)
 constexpr int kKBatch = 6;                // K-steps whose LDS reads are in flight together
-constexpr int kColTiles = kDc / 2 / 32;   // 8 value column tiles per wave (half of 512)
-constexpr int kColTilesA = 4;             // of which phase A runs the first kColTilesA
+constexpr int kColTiles = kDc / 32;       // 16 column tiles of 32 latent columns
 constexpr int kPvAhead = 3;               // value fragments whose loads run ahead
-constexpr int kLoadWords = 18;            // 72 bytes per thread and tile
+constexpr int kStageLanes = 3 * kWave;    // lanes that stage one 16-token block
+constexpr int kLoadChunks = 6;            // 16-byte chunks per staging lane and tile
+constexpr int kLoadWords = 4 * kLoadChunks;
 constexpr float kRaise = 8.0f;
 
 static_assert(kKSteps % kKBatch == 0, "batched K-steps");
 static_assert(kLdsRow % 16 == 0, "16-byte aligned rows");
-// Each 16-token block (18432 bytes) is fetched by 256 threads: 4 x 16 B + 8 B.
-static_assert(kBlockTokens * kRowBytes == 256 * (4 * 16 + 8), "tile load split");
+// Each 16-token block (18432 bytes) is fetched by three waves: 6 x 16 B per lane.
+static_assert(kBlockTokens * kRowBytes == kStageLanes * kLoadChunks * 16, "tile load split");
+
+// Column tiles of value wave w (2 .. 7): [first, first + count).
+__device__ __forceinline__ int value_first_tile(int w) {
+  return w == 2 ? 0 : w == 3 ? 3 : w == 4 ? 6 : w == 5 ? 8 : w == 6 ? 10 : 13;
+}
+__device__ __forceinline__ int value_tile_count(int w) { return (w == 4 || w == 5) ? 2 : 3; }
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
@@ -130,10 +134,9 @@ struct MlaLaunchDev {
 
 struct MlaShared {
   uint8_t tiles[kStages][kTileBytes];
-  float4 xchg[4][4][kWave];        // partial scores of each score wave
-  uint4 pw[2][2][2][kWave];        // [head block][token half][value, remainder][lane]
-  float alpha[2][kBlockHeads];     // rescale of the step, per head
-  float lsum[2][2][kWave];         // final weight sums [head block][K half][lane]
+  // Weights of the tile [step parity][head block][token half][value, remainder][lane]
+  uint4 pw[2][2][2][2][kWave];
+  float alpha[2][2][kBlockHeads];  // rescale of the step [step parity][head block][head]
 };
 
 __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) {
@@ -142,9 +145,7 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = wave_uniform(tid >> 6);
-  const bool score_wave = wave < 4;
-  const int hb = wave & 1;          // head block
-  const int hx = (wave >> 1) & 1;   // K half (score waves) or column half (value waves)
+  const bool score_wave = wave < 2;
   const int r32 = lane & 31;        // MFMA column / row lane: the head, or the token
   const int g = lane >> 5;          // MFMA K group
 
@@ -173,10 +174,9 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   const int ti_new = fused ? rel_new / kTile : -1;  // its tile, -1 for none
   const int r_new = rel_new % kBlockTokens;        // its row in its block
 
-  const int head0 = hg * kHeadsPerGroup + hb * kBlockHeads;
-  const bool active = head0 < a.num_heads;  // blocks past the last head only load
-  const int head = head0 + r32;             // this lane's head
-  const bool head_ok = head < a.num_heads;
+  const int head0 = hg * kHeadsPerGroup;            // first head of the group
+  const bool active0 = head0 < a.num_heads;         // head blocks with heads
+  const bool active1 = head0 + kBlockHeads < a.num_heads;
 
   // The partition's block-table entries (at most 64 blocks), one per lane,
   // read once: tile loads pick theirs with readlane, and `valid` has bit j
@@ -188,128 +188,31 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   if (lane < nblk) entry = a.block_table[static_cast<size_t>(b) * a.max_blocks_per_seq + blk0 + lane];
   const uint64_t valid = __builtin_amdgcn_ballot_w64(entry >= 0 && entry < a.num_blocks);
 
-  // Tile loads: waves 0-3 fetch the tile's first 16-token block, waves 4-7
-  // the second (a block is 16 x 1152 contiguous bytes), each thread 4 chunks
-  // of 16 B and one of 8 B, so every load instruction uses one wave-uniform
-  // buffer resource whose byte count ends at the block's last valid row.
-  const int half = wave >> 2;
-  const int lt = tid & 255;
-
-  // The new row's bytes in the lanes that load them from the cache block
-  // (load_tile's split of a block): at most one 16-byte chunk (c_sel) and
-  // one 8-byte piece (tail_sel) per lane.
-  int c_sel = -1;
-  bool tail_sel = false;
-  uint4 new16 = make_uint4(0u, 0u, 0u, 0u);
-  uint2 new8 = make_uint2(0u, 0u);
-  if (fused && half == ((rel_new / kBlockTokens) & 1)) {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.c_new + static_cast<size_t>(b) * kW);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int qi = lt + 256 * c;
-      if (qi / kChunks == r_new) {
-        c_sel = c;
-        new16 = *reinterpret_cast<const uint4*>(src + (qi % kChunks) * 16);
-      }
-    }
-    const int o = 4 * 256 * 16 + 8 * lt;
-    if (o / kRowBytes == r_new) {
-      tail_sel = true;
-      new8 = *reinterpret_cast<const uint2*>(src + o % kRowBytes);
-    }
-    const int jn = rel_new / kBlockTokens;  // block of the partition
-    if (hg == 0 && ((valid >> jn) & 1)) {
-      // The cache receives the caller's writable buffer on this path.
-      uint8_t* dst = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(a.cache)) +
-                     static_cast<size_t>(__builtin_amdgcn_readlane(entry, jn)) * kBlockTokens * kRowBytes;
-      if (c_sel >= 0) *reinterpret_cast<uint4*>(dst + (lt + 256 * c_sel) * 16) = new16;
-      if (tail_sel) *reinterpret_cast<uint2*>(dst + o) = new8;
-    }
-  }
-  auto load_tile = [&](int ti, uint32_t (&dst)[kLoadWords]) __attribute__((always_inline)) {
-    const int j = 2 * ti + half;  // block of the partition
-    const int t0 = t_begin + j * kBlockTokens;
-    const bool ok = j < nblk && ((valid >> j) & 1);
-    const int blk = ok ? __builtin_amdgcn_readlane(entry, j) : 0;
-    const int nvalid = ok ? min(kBlockTokens, t_end - t0) : 0;
-    const BufRsrc r = make_rsrc(a.cache + static_cast<size_t>(blk) * kBlockTokens * kW,
-                                nvalid * kRowBytes);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      buffer_load_words<4>(dst + 4 * c, r, static_cast<uint32_t>((lt + 256 * c) * 16));
-    buffer_load_words<2>(dst + 16, r, static_cast<uint32_t>(4 * 256 * 16 + 8 * lt));
-  };
-  // Tile tix goes to LDS; the tile holding the new row takes it from c_new.
-  uint32_t st_off[5];  // LDS byte offsets of this thread's pieces of a tile
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int qi = lt + 256 * c;
-    st_off[c] = (half * kBlockTokens + qi / kChunks) * kLdsRow + (qi % kChunks) * 16;
-  }
-  {
-    const int o = 4 * 256 * 16 + 8 * lt;
-    st_off[4] = (half * kBlockTokens + o / kRowBytes) * kLdsRow + o % kRowBytes;
-  }
-  auto store_tile = [&](const uint32_t (&src)[kLoadWords], uint8_t* tile, int tix)
-      __attribute__((always_inline)) {
-    const bool sub = tix == ti_new;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 v = make_uint4(src[4 * c], src[4 * c + 1], src[4 * c + 2], src[4 * c + 3]);
-      if (sub && c == c_sel) v = new16;
-      *reinterpret_cast<uint4*>(tile + opaque(st_off[c])) = v;
-    }
-    uint2 t = make_uint2(src[16], src[17]);
-    if (sub && tail_sel) t = new8;
-    *reinterpret_cast<uint2*>(tile + opaque(st_off[4])) = t;
-  };
-
-  // Register slots of the staging: step t stores tile t + 1 from slot
-  // (t + 1) % 2 into buffer (t + 1) % 3 and starts loading tile t + 3 into
-  // that slot.  Loads past the last tile get a zero-length resource (no
-  // memory traffic).  Steps run in pairs (even step on slot 1, odd on slot
-  // 0), so the order of the loads in flight is the same on every pass and
-  // each store waits only for its own slot.
-  uint32_t pre[2][kLoadWords];
-  load_tile(0, pre[0]);
-  load_tile(1, pre[1]);
-  // Tile 0 into LDS (inside each branch, after the score waves have requested
-  // their query rows, so that both loads are in flight together).
-  auto first_tile = [&]() __attribute__((always_inline)) {
-    store_tile(pre[0], sh.tiles[0], 0);
-    load_tile(2, pre[0]);
-    __syncthreads();
-  };
-
-  const int nsteps = ntiles + 1;  // the value product trails the scores by one tile
-  auto stage = [&](int t, uint32_t (&slot)[kLoadWords]) __attribute__((always_inline)) {
-    store_tile(slot, sh.tiles[(t + 1) % kStages], t + 1);
-    load_tile(t + 3, slot);
-  };
-
   const size_t P = a.num_partitions;
-  const size_t ws_slot = (static_cast<size_t>(b) * a.num_heads + head) * P + p;
+  const int nsteps = ntiles + 1;  // the value product trails the scores by one tile
 
   if (score_wave) {
-    // Q~ as the B operand: lane holds head `head`, K-slots
-    // 288 hx + 16 ks + 8 g .. +7.  (Marked as changed after the load, so
-    // that the compiler keeps it in registers rather than loading it again
-    // inside the loop.)
+    const int hb = wave;                       // head block
+    const bool active = hb == 0 ? active0 : active1;
+    const int head = head0 + hb * kBlockHeads + r32;  // this lane's head
+    const bool head_ok = head < a.num_heads;
+    // Q~ as the B operand: lane holds head `head`, K-slots 16 ks + 8 g .. +7.
+    // (Marked as changed after the load, so that the compiler keeps it in
+    // registers rather than loading it again inside the loop.)
     u32x4_t qf[kKSteps];
     {
       const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
-          a.q + (static_cast<size_t>(b) * a.num_heads + (head_ok ? head : 0)) * kW + hx * (kW / 2));
+          a.q + (static_cast<size_t>(b) * a.num_heads + (head_ok ? head : 0)) * kW);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = head_ok ? qrow[2 * ks + g] : u32x4_t{0u, 0u, 0u, 0u};
     }
-    first_tile();
+    __syncthreads();  // tile 0 staged
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
     float m_run = kMinusBig;  // reference max of this lane's head (log2 units)
     float l_half = 0.f;       // this lane's share of the weight sum
     const float sl2 = a.scale * kLog2e;
-    f32x16_t s;               // this wave's partial scores of the current tile
-    const uint32_t a_off = r32 * kLdsRow + hx * (kRowBytes / 2) + 16 * g;  // A operand row piece
+    const uint32_t a_off = r32 * kLdsRow + 16 * g;  // A operand row piece
 
     // Valid rows of each 16-token half of tile ti (0 for a table entry
     // outside the pool, whose rows were read as zeros and must not get weight).
@@ -319,11 +222,12 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       return ok ? min(kBlockTokens, t_end - t_begin - j * kBlockTokens) : 0;
     };
 
-    auto phase_a = [&](int t) __attribute__((always_inline)) {
+    auto step = [&](int t) __attribute__((always_inline)) {
       if (!active || t >= ntiles) return;
+      const int par = t & 1;
       // A operand: lane holds token r32 of the tile, K-slots as qf.
       const uint8_t* arow = sh.tiles[t % kStages] + opaque(a_off);
-      s = f32x16_t{};
+      f32x16_t s = f32x16_t{};
       uint4 av[kKSteps];
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) av[ks] = *reinterpret_cast<const uint4*>(arow + 32 * ks);
@@ -338,31 +242,16 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
         KVD_SCHED_GROUP(kSchedDsRead, 1);
       }
       KVD_SCHED_GROUP(kSchedMfma, kKBatch);
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        sh.xchg[wave][qd][lane] = make_float4(s[4 * qd], s[4 * qd + 1], s[4 * qd + 2], s[4 * qd + 3]);
-    };
 
-    auto phase_b = [&](int t) __attribute__((always_inline)) {
-      if (!active || t >= ntiles) return;
-      // Both waves of the block form the same sum (K half 0 first), so they
-      // take identical softmax decisions.
-      float z[16];
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const float4 o = sh.xchg[wave ^ 2][qd][lane];
-        const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) z[4 * qd + i] = hx == 0 ? s[4 * qd + i] + ov[i] : ov[i] + s[4 * qd + i];
-      }
       // Register r holds token 8 (r / 4) + 4 g + r % 4 of the tile.
       const int nv0 = half_valid(t, 0), nv1 = half_valid(t, 1);
+      float z[16];
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = 8 * (r / 4) + 4 * g + (r % 4);
         const bool ok = tok < 16 ? tok < nv0 : tok - 16 < nv1;
-        z[r] = ok ? z[r] * sl2 : -INFINITY;
+        z[r] = ok ? s[r] * sl2 : -INFINITY;
         mx = fmaxf(mx, z[r]);
       }
       mx = max_over_halves(mx);
@@ -374,145 +263,227 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
         l_half *= al;
         m_run = mn;
       }
-      if (hx == 0 && g == 0) sh.alpha[hb][r32] = al;
-      // Weights of token half hx (registers 8 hx .. 8 hx + 7, the K-slots of
-      // the value product's K-step hx): a bf16 value and its bf16 remainder
+      if (g == 0) sh.alpha[par][hb][r32] = al;
+      // Weights of token half th (registers 8 th .. 8 th + 7, the K-slots of
+      // the value product's K-step th): a bf16 value and its bf16 remainder
       // (about 16 bits of weight: 8-bit weights move outputs that cancel over
       // a few positions by ~1e-3); the sum takes the fp32 weights.
-      // (A branch per half keeps the register indices static.)
-      auto weights = [&](auto half_c) __attribute__((always_inline)) {
-        constexpr int o = 8 * decltype(half_c)::value;
+#pragma unroll
+      for (int th = 0; th < 2; ++th) {
         uint32_t hi[4], lo[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2_fast(z[o + 2 * e] - m_run);
-          const float p1 = exp2_fast(z[o + 2 * e + 1] - m_run);
+          const float p0 = exp2_fast(z[8 * th + 2 * e] - m_run);
+          const float p1 = exp2_fast(z[8 * th + 2 * e + 1] - m_run);
           l_half += p0 + p1;
           const uint32_t w = pack_bf16x2(p0, p1);
           hi[e] = w;
           lo[e] = pack_bf16x2(p0 - bf16_lo(w), p1 - bf16_hi(w));
         }
-        sh.pw[hb][hx][0][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        sh.pw[hb][hx][1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      };
-      if (hx) weights(std::integral_constant<int, 1>{});
-      else weights(std::integral_constant<int, 0>{});
+        sh.pw[par][hb][th][0][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        sh.pw[par][hb][th][1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
     };
 
     for (int t = 0; t < nsteps; t += 2) {
-      phase_a(t);
-      stage(t, pre[1]);
+      step(t);
       __syncthreads();
-      phase_b(t);
-      __syncthreads();
-      phase_a(t + 1);
-      stage(t + 1, pre[0]);
-      __syncthreads();
-      phase_b(t + 1);
+      step(t + 1);
       __syncthreads();
     }
-    // Weight sum of the head: both K halves, both half-waves.
-    sh.lsum[hb][hx][lane] = l_half;
-    __syncthreads();
-    if (active && hx == 0 && g == 0 && head_ok) {
-      const float l = (sh.lsum[hb][0][lane] + sh.lsum[hb][1][lane]) +
-                      (sh.lsum[hb][0][lane + 32] + sh.lsum[hb][1][lane + 32]);
+    // Weight sum of the head: both half-waves (lanes l and l ^ 32 hold the
+    // same head).
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_half), __float_as_uint(l_half),
+                                               false, false);
+    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (active && g == 0 && head_ok) {
+      const size_t ws_slot = (static_cast<size_t>(b) * a.num_heads + head) * P + p;
       reinterpret_cast<float2*>(a.ws_ml)[ws_slot] = make_float2(m_run, l);
     }
-  } else {
-    // O^T accumulators: lane holds head `head`, latent columns
-    // 256 hx + 32 ct + 8 (r / 4) + 4 g + r % 4 in register r of tile ct.
-    first_tile();
-    f32x16_t acc[kColTiles];
-#pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) acc[ct] = f32x16_t{};
-    uint4 pv[2][2];  // weights of the tile: [token half][value, remainder]
+    return;
+  }
 
-    // A operand of column tile ct, token half j: lane (row r32, K group g)
-    // gets tokens 16 j + 4 g + 0..3 and 16 j + 8 + 4 g + 0..3 of latent
-    // column 256 hx + 32 ct + r32 from two transpose loads; within each
-    // 16-lane group, lane i supplies row (i / 4) of the four and columns
-    // 4 (i % 4) .. +3 of the group's sixteen.
-    const int gi = lane & 15;
-    const uint32_t v_off = (4 * g + (gi >> 2)) * kLdsRow +
-                           (hx * (kDc / 2) + 16 * ((lane >> 4) & 1) + 4 * (gi & 3)) * 2;
-    // The transpose loads run kPvAhead fragments ahead of their MFMAs.
-    auto pv_tiles = [&](const uint8_t* tile, auto ct0_c, auto ct1_c) __attribute__((always_inline)) {
-      constexpr int ct0 = decltype(ct0_c)::value, ct1 = decltype(ct1_c)::value;
-      const uint8_t* vb = tile + opaque(v_off);
-      uint2 w[ct1 - ct0][2][2];
+  // A operand of column tile ct, token half j: lane (row r32, K group g)
+  // gets tokens 16 j + 4 g + 0..3 and 16 j + 8 + 4 g + 0..3 of latent
+  // column 32 ct + r32 from two transpose loads; within each 16-lane group,
+  // lane i supplies row (i / 4) of the four and columns 4 (i % 4) .. +3 of
+  // the group's sixteen.
+  const int gi = lane & 15;
+  const int ct0 = value_first_tile(wave);
+  const uint32_t v_off = (4 * g + (gi >> 2)) * kLdsRow +
+                         (32 * ct0 + 16 * ((lane >> 4) & 1) + 4 * (gi & 3)) * 2;
+
+  // NCT column tiles from ct0: O^T accumulators acc[head block][tile], lane
+  // holds head r32 of the block, latent columns 32 (ct0 + ct) + 8 (r / 4) +
+  // 4 g + r % 4 in register r.
+  // (The whole value path, staging included, is instantiated once per column
+  // tile count, so that no register of one instance lives across the other.)
+  auto run = [&](auto nct_c) __attribute__((always_inline)) {
+    constexpr int NCT = decltype(nct_c)::value;
+    // ---- Value waves: staging of the tiles, then the value products.
+    // Tile loads: waves 2-4 fetch the tile's first 16-token block, waves 5-7
+    // the second (a block is 16 x 1152 contiguous bytes), each lane 6 chunks of
+    // 16 B, so every load instruction uses one wave-uniform buffer resource
+    // whose byte count ends at the block's last valid row.
+    const int half = (wave - 2) / 3;
+    const int lt = ((wave - 2) % 3) * kWave + lane;
+
+    // The new row's bytes in the lane that loads them from the cache block (at
+    // most one 16-byte chunk per lane: a row is 72 chunks, a lane's chunks are
+    // 192 apart).
+    int c_sel = -1;
+    uint4 new16 = make_uint4(0u, 0u, 0u, 0u);
+    if (fused && half == ((rel_new / kBlockTokens) & 1)) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.c_new + static_cast<size_t>(b) * kW);
 #pragma unroll
-      for (int ct = ct0; ct < ct1; ++ct)
+      for (int c = 0; c < kLoadChunks; ++c) {
+        const int qi = lt + kStageLanes * c;
+        if (qi / kChunks == r_new) {
+          c_sel = c;
+          new16 = *reinterpret_cast<const uint4*>(src + (qi % kChunks) * 16);
+        }
+      }
+      const int jn = rel_new / kBlockTokens;  // block of the partition
+      if (hg == 0 && c_sel >= 0 && ((valid >> jn) & 1)) {
+        // The cache receives the caller's writable buffer on this path.
+        uint8_t* dst = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(a.cache)) +
+                       static_cast<size_t>(__builtin_amdgcn_readlane(entry, jn)) * kBlockTokens * kRowBytes;
+        *reinterpret_cast<uint4*>(dst + (lt + kStageLanes * c_sel) * 16) = new16;
+      }
+    }
+    auto load_tile = [&](int ti, uint32_t (&dst)[kLoadWords]) __attribute__((always_inline)) {
+      const int j = 2 * ti + half;  // block of the partition
+      const int t0 = t_begin + j * kBlockTokens;
+      const bool ok = j < nblk && ((valid >> j) & 1);
+      const int blk = ok ? __builtin_amdgcn_readlane(entry, j) : 0;
+      const int nvalid = ok ? min(kBlockTokens, t_end - t0) : 0;
+      const BufRsrc r = make_rsrc(a.cache + static_cast<size_t>(blk) * kBlockTokens * kW,
+                                  nvalid * kRowBytes);
+#pragma unroll
+      for (int c = 0; c < kLoadChunks; ++c)
+        buffer_load_words<4>(dst + 4 * c, r, static_cast<uint32_t>((lt + kStageLanes * c) * 16));
+    };
+    uint32_t st_off[kLoadChunks];  // LDS byte offsets of this lane's pieces of a tile
+#pragma unroll
+    for (int c = 0; c < kLoadChunks; ++c) {
+      const int qi = lt + kStageLanes * c;
+      st_off[c] = (half * kBlockTokens + qi / kChunks) * kLdsRow + (qi % kChunks) * 16;
+    }
+    // Tile tix goes to LDS; the tile holding the new row takes it from c_new.
+    auto store_tile = [&](const uint32_t (&src)[kLoadWords], uint8_t* tile, int tix)
+        __attribute__((always_inline)) {
+      const bool sub = tix == ti_new;
+#pragma unroll
+      for (int c = 0; c < kLoadChunks; ++c) {
+        uint4 v = make_uint4(src[4 * c], src[4 * c + 1], src[4 * c + 2], src[4 * c + 3]);
+        if (sub && c == c_sel) v = new16;
+        *reinterpret_cast<uint4*>(tile + opaque(st_off[c])) = v;
+      }
+    };
+
+    // Register slots of the staging: step t stores tile t + 1 from slot
+    // (t + 1) % 2 into buffer (t + 1) % 3 and starts loading tile t + 3 into
+    // that slot.  Loads past the last tile get a zero-length resource (no
+    // memory traffic).  Steps run in pairs (even step on slot 1, odd on slot
+    // 0), so the order of the loads in flight is the same on every pass and
+    // each store waits only for its own slot.
+    uint32_t pre[2][kLoadWords];
+    load_tile(0, pre[0]);
+    load_tile(1, pre[1]);
+    store_tile(pre[0], sh.tiles[0], 0);
+    load_tile(2, pre[0]);
+    __syncthreads();  // tile 0 staged
+
+    auto stage = [&](int t, uint32_t (&slot)[kLoadWords]) __attribute__((always_inline)) {
+      store_tile(slot, sh.tiles[(t + 1) % kStages], t + 1);
+      load_tile(t + 3, slot);
+    };
+
+    f32x16_t acc[2][NCT];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[h][ct] = f32x16_t{};
+
+    auto step = [&](int t) __attribute__((always_inline)) {
+      if (!active0 || t < 1 || t > ntiles) return;
+      const int par = (t - 1) & 1;
+      const float al0 = sh.alpha[par][0][r32], al1 = sh.alpha[par][1][r32];
+      uint4 pv[2][2][2];  // weights of the tile: [head block][token half][value, remainder]
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int vr = 0; vr < 2; ++vr) pv[h][j][vr] = sh.pw[par][h][j][vr][lane];
+      if (__builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f)) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[0][ct][r] *= al0;
+            acc[1][ct][r] *= al1;
+          }
+      }
+      // The transpose loads run kPvAhead fragments ahead of their MFMAs.
+      const uint8_t* vb = sh.tiles[(t - 1) % kStages] + opaque(v_off);
+      uint2 w[NCT][2][2];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
-            w[ct - ct0][j][hh] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            w[ct][j][hh] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_s16x4_t*)(vb + (16 * j + 8 * hh) * kLdsRow + 64 * ct)));
 #pragma unroll
-      for (int ct = ct0; ct < ct1; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint2 w0 = w[ct - ct0][j][0], w1 = w[ct - ct0][j][1];
+          const uint2 w0 = w[ct][j][0], w1 = w[ct][j][1];
           const bf16x8_t va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
-          acc[ct] = mfma32(va, as_bf16x8(pv[j][0]), acc[ct]);
-          acc[ct] = mfma32(va, as_bf16x8(pv[j][1]), acc[ct]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            acc[h][ct] = mfma32(va, as_bf16x8(pv[h][j][0]), acc[h][ct]);
+            acc[h][ct] = mfma32(va, as_bf16x8(pv[h][j][1]), acc[h][ct]);
+          }
         }
-      constexpr int frags = 2 * (ct1 - ct0);
+      constexpr int frags = 2 * NCT;
       KVD_SCHED_GROUP(kSchedDsRead, 2 * kPvAhead);
 #pragma unroll
       for (int f = 0; f < frags - kPvAhead; ++f) {
-        KVD_SCHED_GROUP(kSchedMfma, 2);
+        KVD_SCHED_GROUP(kSchedMfma, 4);
         KVD_SCHED_GROUP(kSchedDsRead, 2);
       }
-      KVD_SCHED_GROUP(kSchedMfma, 2 * kPvAhead);
-    };
-
-    auto phase_a = [&](int t) __attribute__((always_inline)) {
-      if (!active || t < 1 || t > ntiles) return;
-      const float al = sh.alpha[hb][r32];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        pv[j][0] = sh.pw[hb][j][0][lane];
-        pv[j][1] = sh.pw[hb][j][1][lane];
-      }
-      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
-#pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[ct][r] *= al;
-      }
-      pv_tiles(sh.tiles[(t - 1) % kStages], std::integral_constant<int, 0>{},
-               std::integral_constant<int, kColTilesA>{});
-    };
-    auto phase_b = [&](int t) __attribute__((always_inline)) {
-      if (!active || t < 1 || t > ntiles) return;
-      pv_tiles(sh.tiles[(t - 1) % kStages], std::integral_constant<int, kColTilesA>{},
-               std::integral_constant<int, kColTiles>{});
+      KVD_SCHED_GROUP(kSchedMfma, 4 * kPvAhead);
     };
 
     for (int t = 0; t < nsteps; t += 2) {
-      phase_a(t);
+      step(t);
       stage(t, pre[1]);
       __syncthreads();
-      phase_b(t);
-      __syncthreads();
-      phase_a(t + 1);
+      step(t + 1);
       stage(t + 1, pre[0]);
       __syncthreads();
-      phase_b(t + 1);
-      __syncthreads();
     }
-    __syncthreads();  // matches the score waves' weight-sum exchange
-    if (!active || !head_ok) return;
-    float* orow = a.ws_o + ws_slot * kDc + hx * (kDc / 2) + 4 * g;
+    if (!active0) return;
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct)
+    for (int h = 0; h < 2; ++h) {
+      const int head = head0 + h * kBlockHeads + r32;
+      if (head >= a.num_heads) continue;
+      const size_t ws_slot = (static_cast<size_t>(b) * a.num_heads + head) * P + p;
+      float* orow = a.ws_o + ws_slot * kDc + 32 * ct0 + 4 * g;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<float4*>(orow + 32 * ct + 8 * qd) =
-            make_float4(acc[ct][4 * qd], acc[ct][4 * qd + 1], acc[ct][4 * qd + 2], acc[ct][4 * qd + 3]);
-  }
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<float4*>(orow + 32 * ct + 8 * qd) =
+              make_float4(acc[h][ct][4 * qd], acc[h][ct][4 * qd + 1], acc[h][ct][4 * qd + 2],
+                          acc[h][ct][4 * qd + 3]);
+    }
+  };
+  if (value_tile_count(wave) == 2) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 3>{});
 }
 
 }  // namespace

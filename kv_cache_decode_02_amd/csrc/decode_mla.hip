@@ -159,10 +159,23 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   const int p = pp % a.num_partitions;
   const int b = pp / a.num_partitions;
 
+  // The partition's block-table entries (at most 64 blocks), one per lane,
+  // are requested together with the length, before it is known: lane k
+  // reads entry blk0 + k of the row (0 past the row's end) and the entries
+  // past the partition's last block are dropped below.
+  const int t_begin = p * a.partition_tokens;
+  const int blk0 = t_begin / kBlockTokens;
+  int entry;
+  {
+    const int32_t* trow = a.block_table + static_cast<size_t>(b) * a.max_blocks_per_seq;
+    const int left = wave_uniform(min(max(0, a.max_blocks_per_seq - blk0), kWave));
+    const BufRsrc rt = make_rsrc(trow + min(blk0, a.max_blocks_per_seq), left * 4);
+    entry = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(rt, 4 * lane, 0, 0));
+  }
   const int len_in = a.seq_lens[b];
+  asm volatile("" ::: "memory");  // (both requests before either wait)
   int len = min(len_in, a.max_seq_len);
   len = min(len, a.max_blocks_per_seq * kBlockTokens);
-  const int t_begin = p * a.partition_tokens;
   if (len <= t_begin) return;
   const int t_end = min(len, t_begin + a.partition_tokens);
   const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
@@ -178,15 +191,15 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   const bool active0 = head0 < a.num_heads;         // head blocks with heads
   const bool active1 = head0 + kBlockHeads < a.num_heads;
 
-  // The partition's block-table entries (at most 64 blocks), one per lane,
-  // read once: tile loads pick theirs with readlane, and `valid` has bit j
-  // set when block j of the partition lies inside the pool.  No memory reads
+  // Tile loads pick their block ids with readlane, and `valid` has bit j set
+  // when block j of the partition lies inside the pool.  No memory reads
   // remain in the tile loop besides the tile loads themselves.
-  const int blk0 = t_begin / kBlockTokens;
+  // (Formed in each branch after its first requests: it waits for the table.)
   const int nblk = (t_end - t_begin + kBlockTokens - 1) / kBlockTokens;
-  int entry = -1;
-  if (lane < nblk) entry = a.block_table[static_cast<size_t>(b) * a.max_blocks_per_seq + blk0 + lane];
-  const uint64_t valid = __builtin_amdgcn_ballot_w64(entry >= 0 && entry < a.num_blocks);
+  auto valid_blocks = [&]() __attribute__((always_inline)) {
+    if (lane >= nblk) entry = -1;
+    return __builtin_amdgcn_ballot_w64(entry >= 0 && entry < a.num_blocks);
+  };
 
   const size_t P = a.num_partitions;
   const int nsteps = ntiles + 1;  // the value product trails the scores by one tile
@@ -197,15 +210,17 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
     const int head = head0 + hb * kBlockHeads + r32;  // this lane's head
     const bool head_ok = head < a.num_heads;
     // Q~ as the B operand: lane holds head `head`, K-slots 16 ks + 8 g .. +7.
-    // (Marked as changed after the load, so that the compiler keeps it in
-    // registers rather than loading it again inside the loop.)
+    // A lane past the last head takes head 0's row; its results are never
+    // written.  (Marked as changed after the load, so that the compiler keeps
+    // it in registers rather than loading it again inside the loop.)
     u32x4_t qf[kKSteps];
     {
       const u32x4_t* qrow = reinterpret_cast<const u32x4_t*>(
           a.q + (static_cast<size_t>(b) * a.num_heads + (head_ok ? head : 0)) * kW);
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = head_ok ? qrow[2 * ks + g] : u32x4_t{0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = qrow[2 * ks + g];
     }
+    const uint64_t valid = valid_blocks();
     __syncthreads();  // tile 0 staged
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
@@ -327,6 +342,7 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
     // whose byte count ends at the block's last valid row.
     const int half = (wave - 2) / 3;
     const int lt = ((wave - 2) % 3) * kWave + lane;
+    const uint64_t valid = valid_blocks();
 
     // The new row's bytes in the lane that loads them from the cache block (at
     // most one 16-byte chunk per lane: a row is 72 chunks, a lane's chunks are

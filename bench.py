@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--workload", default="gqa_llama3_8b",
                     choices=["gqa_llama3_8b", "mha_llama2_7b", "long_gqa_split", "tiny",
                              "mla_deepseek_v2", "gqa_llama3_8b_int8", "gqa_llama3_8b_fp8",
-                             "prefill_llama3_8b", "stream_read"])
+                             "prefill_llama3_8b", "stream_read", "lds_read"])
     ap.add_argument("--replicas", type=int, default=4,
                     help="MLA: rotate over this many copies of the latent cache so the "
                          "timed reads come from HBM, not the 256 MB Infinity Cache")
@@ -656,6 +656,44 @@ def main_stream(args, kvd):
                                    "frac": c["frac_of_peak"], "traffic": None}}), flush=True)
 
 
+def main_lds(args, kvd):
+    """The LDS-read probe alone: one workgroup of eight waves per compute unit
+    reading its LDS, for 16-byte and for transposing 8-byte reads."""
+    import torch
+    groups = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4096
+    cycles = torch.zeros(groups, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(kvd.lds_read_sink_bytes(groups), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    launches = max(args.steps, 20)
+    legs = {}
+    for mode, name in ((0, "b128"), (1, "tr_b64")):
+        for _ in range(3):
+            kvd.lds_read(mode, groups, iters, cycles, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(launches):
+            kvd.lds_read(mode, groups, iters, cycles, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / launches
+        nbytes = kvd.lds_read_bytes(mode, groups, iters)
+        cyc = float(cycles.double().mean())
+        legs[name] = {"bytes_per_launch": nbytes, "ms_per_launch": round(ms, 5),
+                      "TBps_all_cus": round(nbytes / (ms / 1e3) / 1e12, 2),
+                      "bytes_per_cycle_per_cu": round(nbytes / groups / cyc, 1),
+                      "loop_cycles_per_cu": round(cyc, 0)}
+    print(json.dumps({"metric": "LDS read bytes per cycle and compute unit, 1 MI355X",
+                      "value": legs["b128"]["bytes_per_cycle_per_cu"], "unit": "B/cycle/CU",
+                      "n_gpus": 1, "steps": launches, "warmup": 3,
+                      "ms_per_step": legs["b128"]["ms_per_launch"], "higher_is_better": True,
+                      "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+                      "config": {"workload": "lds_read", "groups": groups, "iters": iters,
+                                 "threads_per_group": 512},
+                      "legs": legs}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -674,6 +712,9 @@ def main():
 
     if args.workload == "stream_read":
         main_stream(args, kvd)
+        return
+    if args.workload == "lds_read":
+        main_lds(args, kvd)
         return
     cfg = config(args.workload)
     if cfg["kind"] == "mla":

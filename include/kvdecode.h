@@ -337,6 +337,30 @@ size_t kvd_stream_read_sink_bytes(void);
 int kvd_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
 
 /*
+ * kvd_lds_read -- measurement aid, not a step of the decode: `groups`
+ * workgroups of 512 threads (eight waves, the shape of the MLA kernel's
+ * workgroup) each read a 64 KiB LDS array `iters` times, eight reads in
+ * flight per lane, without bank conflicts, so that the rate gives one
+ * compute unit's sustained LDS read bandwidth for the kinds of read that
+ * feed the MLA and prefill kernels' MFMAs (context for their step times).
+ *   mode    0: 16-byte reads (ds_read_b128); 1: 8-byte transposing reads of
+ *           16-bit elements (ds_read_b64_tr_b16)
+ *   groups  1 .. 65535 (one per compute unit measures one unit's rate)
+ *   iters   1 .. 2^24; kvd_lds_read_bytes() gives the bytes read per launch
+ *   cycles  device memory, 8-byte aligned, `groups` uint64 words: the shader
+ *           clock cycles of each workgroup's read loop (wave 0's count)
+ *   sink    device memory of at least kvd_lds_read_sink_bytes(groups)
+ *           bytes; a word of it is written only if a thread's fold of its
+ *           reads equals a fixed sentinel
+ * Returns KVD_OK, KVD_ERR_UNSUPPORTED (mode), KVD_ERR_SHAPE, KVD_ERR_NULL,
+ * KVD_ERR_WORKSPACE (sink too small) or KVD_ERR_HIP.  Asynchronous on stream.
+ */
+size_t kvd_lds_read_sink_bytes(int groups);
+long long kvd_lds_read_bytes(int mode, int groups, int iters);
+int kvd_lds_read(int mode, int groups, int iters, void* cycles, void* sink, size_t sink_bytes,
+                 void* stream);
+
+/*
  * decode_attn_mla -- absorbed multi-head latent attention decode (bf16).
  *
  * The cache keeps one row per token: the latent c_t (d_c values) followed by

@@ -22,6 +22,9 @@ from ._native import (
     decode_attn_noalloc_scratch_bytes,
     stream_read,
     stream_read_sink_bytes,
+    lds_read,
+    lds_read_sink_bytes,
+    lds_read_bytes,
     decode_attn_paged_window,
     decode_attn_paged_window_partials,
     decode_attn_merge,
@@ -55,7 +58,7 @@ __all__ = [
     "KvdError", "kv_append_paged", "decode_attn_paged", "decode_attn_paged_partials",
     "decode_attn_paged_append", "decode_attn_paged_append_partials",
     "decode_attn_paged_append_noalloc", "decode_attn_noalloc_scratch_bytes",
-    "stream_read", "stream_read_sink_bytes",
+    "stream_read", "stream_read_sink_bytes", "lds_read", "lds_read_sink_bytes", "lds_read_bytes",
     "decode_attn_paged_window", "decode_attn_paged_window_partials",
     "decode_attn_merge", "decode_attn_workspace_bytes", "decode_attn_partition_tokens",
     "alloc_workspace", "decode_attn_mla", "decode_attn_mla_partials",

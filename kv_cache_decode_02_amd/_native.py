@@ -60,6 +60,12 @@ lib.kvd_stream_read_sink_bytes.restype = _sz
 lib.kvd_stream_read_sink_bytes.argtypes = []
 lib.kvd_stream_read.restype = _i
 lib.kvd_stream_read.argtypes = [_vp, _sz, _vp, _sz, _vp]
+lib.kvd_lds_read_sink_bytes.restype = _sz
+lib.kvd_lds_read_sink_bytes.argtypes = [_i]
+lib.kvd_lds_read_bytes.restype = ctypes.c_longlong
+lib.kvd_lds_read_bytes.argtypes = [_i, _i, _i]
+lib.kvd_lds_read.restype = _i
+lib.kvd_lds_read.argtypes = [_i, _i, _i, _vp, _vp, _sz, _vp]
 _MLA_ARGS = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 lib.decode_attn_mla.restype = _i
 lib.decode_attn_mla.argtypes = [_vp] + _MLA_ARGS
@@ -413,6 +419,29 @@ def stream_read(src, sink, stream=None):
 
 def stream_read_sink_bytes():
     return int(lib.kvd_stream_read_sink_bytes())
+
+
+def lds_read(mode, groups, iters, cycles, sink, stream=None):
+    """Measurement aid: ``groups`` workgroups read their LDS ``iters`` times
+    (mode 0: 16-byte reads, 1: 8-byte transposing reads).  ``cycles`` is a
+    device int64 tensor of ``groups`` words (shader clock cycles of each
+    workgroup's read loop); ``sink`` a device tensor of at least
+    lds_read_sink_bytes(groups) bytes."""
+    _need(cycles, "cycles", dtype=torch.int64)
+    _need(sink, "sink", like=cycles)
+    if cycles.numel() < groups:
+        raise KvdError(f"kvd_lds_read: cycles holds {cycles.numel()} words, need {groups}")
+    _check(lib.kvd_lds_read(int(mode), int(groups), int(iters), _ptr(cycles), _ptr(sink),
+                            sink.numel() * sink.element_size(), _stream(stream)),
+           "kvd_lds_read")
+
+
+def lds_read_sink_bytes(groups):
+    return int(lib.kvd_lds_read_sink_bytes(int(groups)))
+
+
+def lds_read_bytes(mode, groups, iters):
+    return int(lib.kvd_lds_read_bytes(int(mode), int(groups), int(iters)))
 
 
 def decode_attn_merge(out, seq_lens, num_kv_heads, max_seq_len, workspace, partition_tokens=0,

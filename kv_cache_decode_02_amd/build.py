@@ -25,7 +25,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "block_pool.cpp", "validate.cpp", "append.hip", "decode_paged.hip", "decode_merge.hip",
            "decode_mla.hip", "prefill_paged.hip", "scratch.hip",
-           "stream_read.hip"]
+           "stream_read.hip", "lds_read.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}"]

@@ -11,6 +11,7 @@
 
 #include "../../include/kvdecode.h"
 #include "kvd_internal.h"
+#include "kvd_probe.h"
 #include "kvd_validate.h"
 
 namespace kvd {
@@ -532,6 +533,27 @@ int kvd_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes
   if (sink_bytes < kvd_stream_read_sink_bytes()) return KVD_ERR_WORKSPACE;
   return hip_status(launch_stream_read(src, bytes, static_cast<uint32_t*>(sink),
                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t kvd_lds_read_sink_bytes(int groups) {
+  return groups < 1 ? 0 : static_cast<size_t>(groups) * lds_read_threads() * sizeof(uint32_t);
+}
+
+long long kvd_lds_read_bytes(int mode, int groups, int iters) {
+  if ((mode != 0 && mode != 1) || groups < 1 || iters < 0) return 0;
+  return static_cast<long long>(groups) * lds_read_threads() * iters *
+         lds_read_bytes_per_lane_iter(mode);
+}
+
+int kvd_lds_read(int mode, int groups, int iters, void* cycles, void* sink, size_t sink_bytes,
+                 void* stream) {
+  if (mode != 0 && mode != 1) return KVD_ERR_UNSUPPORTED;
+  if (groups < 1 || groups > 65535 || iters < 1 || iters > (1 << 24)) return KVD_ERR_SHAPE;
+  if (!cycles || !sink) return KVD_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(cycles) & 7u) != 0) return KVD_ERR_SHAPE;
+  if (sink_bytes < kvd_lds_read_sink_bytes(groups)) return KVD_ERR_WORKSPACE;
+  return hip_status(launch_lds_read(mode, groups, iters, static_cast<unsigned long long*>(cycles),
+                                    static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)));
 }
 
 static int append_bytes(void* k_cache, void* v_cache, float* v_scale, const void* k_new,

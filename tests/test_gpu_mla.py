@@ -55,6 +55,11 @@ CASES = [
     ("h16-one-wave", dict(B=2, H=16, lens=[31, 500], std=1.0, pt=32)),
     ("h64-pt256", dict(B=2, H=64, lens=[256, 257], std=0.5, pt=256)),
     ("h80-partial-group", dict(B=2, H=80, lens=[90, 300], std=1.0, pt=0)),
+    # The second 32-head block of a 64-head group half filled, then empty.
+    ("h48-half-block", dict(B=2, H=48, lens=[129, 1024], std=1.0, pt=96)),
+    ("h32-one-block", dict(B=3, H=32, lens=[2, 95, 640], std=1.0, pt=0)),
+    # Many 32-token tiles per partition (odd and even counts), long rows.
+    ("h128-long-odd-tiles", dict(B=2, H=128, lens=[2015, 4096], std=1 / 24, pt=1024)),
 ]
 
 

@@ -32,3 +32,30 @@ def test_stream_read_rejects_bad_sizes():
         kvd.stream_read(src, sink)                  # not a multiple of 16
     with pytest.raises(kvd.KvdError):
         kvd.stream_read(src[:16], sink[:16])        # sink too small
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["b128", "tr_b64"])
+def test_lds_read_runs_and_counts_cycles(mode):
+    groups, iters = 8, 64
+    cycles = torch.zeros(groups, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(kvd.lds_read_sink_bytes(groups), dtype=torch.uint8, device="cuda")
+    kvd.lds_read(mode, groups, iters, cycles, sink)
+    torch.cuda.synchronize()
+    c = cycles.cpu()
+    # Every workgroup ran its read loop: at least one cycle per read
+    # instruction of a wave (8 in flight per iteration).
+    assert (c >= 8 * iters).all(), c
+    assert kvd.lds_read_bytes(mode, groups, iters) == groups * 512 * iters * 8 * (16 if mode == 0 else 8)
+
+
+def test_lds_read_rejects_bad_arguments():
+    cycles = torch.zeros(4, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(kvd.lds_read_sink_bytes(4), dtype=torch.uint8, device="cuda")
+    with pytest.raises(kvd.KvdError):
+        kvd.lds_read(2, 4, 8, cycles, sink)          # no such mode
+    with pytest.raises(kvd.KvdError):
+        kvd.lds_read(0, 4, 0, cycles, sink)          # no iterations
+    with pytest.raises(kvd.KvdError):
+        kvd.lds_read(0, 8, 8, cycles, sink)          # cycles holds 4 words
+    with pytest.raises(kvd.KvdError):
+        kvd.lds_read(0, 4, 8, cycles, sink[:16])     # sink too small

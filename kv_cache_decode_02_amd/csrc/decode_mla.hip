@@ -262,12 +262,20 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       const int nv0 = half_valid(t, 0), nv1 = half_valid(t, 1);
       float z[16];
       float mx = -INFINITY;
+      if (nv0 == kBlockTokens && nv1 == kBlockTokens) {  // (every position valid)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = 8 * (r / 4) + 4 * g + (r % 4);
-        const bool ok = tok < 16 ? tok < nv0 : tok - 16 < nv1;
-        z[r] = ok ? s[r] * sl2 : -INFINITY;
-        mx = fmaxf(mx, z[r]);
+        for (int r = 0; r < 16; ++r) {
+          z[r] = s[r] * sl2;
+          mx = fmaxf(mx, z[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = 8 * (r / 4) + 4 * g + (r % 4);
+          const bool ok = tok < 16 ? tok < nv0 : tok - 16 < nv1;
+          z[r] = ok ? s[r] * sl2 : -INFINITY;
+          mx = fmaxf(mx, z[r]);
+        }
       }
       mx = max_over_halves(mx);
       const bool up = mx > m_run + kRaise;
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
           const float p0 = exp2_fast(z[8 * th + 2 * e] - m_run);
           const float p1 = exp2_fast(z[8 * th + 2 * e + 1] - m_run);
           l_half += p0 + p1;
-          const uint32_t w = pack_bf16x2(p0, p1);
+          const uint32_t w = opaque(pack_bf16x2(p0, p1));
           hi[e] = w;
           lo[e] = pack_bf16x2(p0 - bf16_lo(w), p1 - bf16_hi(w));
         }

@@ -1320,8 +1320,8 @@ size_t device_lds_per_cu() {
 
 // Balanced split: as many workgroups as are resident at once: 4 * WPE
 // wavefronts per compute unit in workgroups of WG waves, or fewer when their
-// LDS (the static wave slices and the two batch prefixes) does not fit that
-// many (large batches on four-wave workgroups).
+// LDS (the static wave slices, the two batch prefixes and the lengths) does
+// not fit that many (large batches).
 template <class W, int WPE, int WG>
 hipError_t launch_balanced(const PagedLaunch& a, hipStream_t stream) {
   const size_t lds = (3 * static_cast<size_t>(a.batch) + 2) * sizeof(int);

@@ -482,12 +482,14 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       KVD_SCHED_GROUP(kSchedMfma, 4 * kPvAhead);
     };
 
+    // Staging first: the products of the value waves beside the score waves
+    // then reach the matrix unit after the score MFMA chain has started.
     for (int t = 0; t < nsteps; t += 2) {
-      step(t);
       stage(t, pre[1]);
+      step(t);
       __syncthreads();
-      step(t + 1);
       stage(t + 1, pre[0]);
+      step(t + 1);
       __syncthreads();
     }
     if (!active0) return;

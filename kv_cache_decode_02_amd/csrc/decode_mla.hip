@@ -18,11 +18,11 @@
 //                       writes the weights of its block to LDS;
 //     value waves 2-7   (a range of 32-column tiles of the latent, both head
 //                       blocks): the unnormalised output of 64 heads x their
-//                       columns in registers, fed by those weights.  Waves
-//                       4 and 5 share a SIMD with the score waves (wave w
-//                       runs beside wave w + 4) and take two column tiles,
-//                       the others three, so every SIMD issues about the
-//                       same number of MFMAs per tile.
+//                       columns in registers, fed by those weights.  Wave w
+//                       runs beside wave w + 4 on a SIMD; waves 2-5 take
+//                       three column tiles and 6-7 two, which with the order
+//                       of each wave's staging and products balances the
+//                       SIMDs' matrix units over a tile.
 //   Tokens come in tiles of 32 (two 16-token blocks), loaded once per
 //   workgroup through the block table (rows past the sequence end read as
 //   zeros) by the value waves, stored token-major in LDS and read by all 8
@@ -84,9 +84,9 @@ static_assert(kBlockTokens * kRowBytes == kStageLanes * kLoadChunks * 16, "tile 
 
 // Column tiles of value wave w (2 .. 7): [first, first + count).
 __device__ __forceinline__ int value_first_tile(int w) {
-  return w == 2 ? 0 : w == 3 ? 3 : w == 4 ? 6 : w == 5 ? 8 : w == 6 ? 10 : 13;
+  return w == 2 ? 0 : w == 3 ? 3 : w == 4 ? 6 : w == 5 ? 9 : w == 6 ? 12 : 14;
 }
-__device__ __forceinline__ int value_tile_count(int w) { return (w == 4 || w == 5) ? 2 : 3; }
+__device__ __forceinline__ int value_tile_count(int w) { return (w == 6 || w == 7) ? 2 : 3; }
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
@@ -482,14 +482,18 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       KVD_SCHED_GROUP(kSchedMfma, 4 * kPvAhead);
     };
 
-    // Staging first: the products of the value waves beside the score waves
-    // then reach the matrix unit after the score MFMA chain has started.
+    // Waves 2-5 stage first, so that the products of waves 4-5 reach the
+    // matrix unit after the score MFMA chain beside them has started; waves
+    // 6-7 (two column tiles) run their products first, while waves 2-3 on
+    // their SIMDs stage.
     for (int t = 0; t < nsteps; t += 2) {
+      if constexpr (NCT == 2) step(t);
       stage(t, pre[1]);
-      step(t);
+      if constexpr (NCT != 2) step(t);
       __syncthreads();
+      if constexpr (NCT == 2) step(t + 1);
       stage(t + 1, pre[0]);
-      step(t + 1);
+      if constexpr (NCT != 2) step(t + 1);
       __syncthreads();
     }
     if (!active0) return;

@@ -71,11 +71,15 @@ __device__ __forceinline__ void merge_pieces(const float2* ml, const float* o, i
     den = w_lane * v.y;
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) den += shfl_xor_f(den, s);
+    // (An empty piece, weight 0, may hold no row values at all: it is
+    // skipped rather than multiplied by 0.)
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
       const float w = __shfl(w_lane, k, kWave);
+      if (w != 0.f) {
 #pragma unroll
-      for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);
+        for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);
+      }
     }
     return;
   }

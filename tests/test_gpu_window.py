@@ -77,3 +77,31 @@ def test_window_covering_everything_equals_full_decode():
                                        inp.max_seq_len, inp.max_seq_len)
     torch.cuda.synchronize()
     assert torch.equal(full.view(torch.int16), win.view(torch.int16))
+
+
+def test_merge_never_reads_rows_of_empty_pieces():
+    # Fixed partitions wholly before the window are empty pieces (l = 0).
+    # The merge gives them no weight and must not read their rows: with
+    # those rows overwritten by NaN the output stays bit for bit the same.
+    log("merge skips empty pieces")
+    B, Hq, Hkv, d, pt, W = 4, 32, 8, 128, 256, 33
+    inp = make_paged_decode(np.random.default_rng(91), B, Hq, Hkv, d, [40, 700, 3000, 513])
+    dev = Paged(inp)
+    kvd.kv_append_paged(dev.k_cache, dev.v_cache, dev.k_new, dev.v_new, dev.table, dev.seq)
+    ws = kvd.alloc_workspace(B, Hq, Hkv, d, inp.max_seq_len, pt)
+    kvd.decode_attn_paged_window_partials(dev.q, dev.k_cache, dev.v_cache, dev.table, dev.seq,
+                                          inp.max_seq_len, W, ws, partition_tokens=pt)
+    clean = torch.empty_like(dev.q)
+    kvd.decode_attn_merge(clean, dev.seq, Hkv, inp.max_seq_len, ws, partition_tokens=pt)
+    P = -(-inp.max_seq_len // pt)
+    f = ws.view(torch.float32)
+    o = f[:B * Hq * P * d].view(B * Hq * P, d)
+    ml_at = -(-(B * Hq * P * d * 4) // 256) * 256 // 4
+    ml = f[ml_at:ml_at + B * Hq * P * 2].view(B * Hq * P, 2)
+    empty = ml[:, 1] == 0
+    assert int(empty.sum()) > 0
+    o[empty] = float("nan")
+    poisoned = torch.empty_like(dev.q)
+    kvd.decode_attn_merge(poisoned, dev.seq, Hkv, inp.max_seq_len, ws, partition_tokens=pt)
+    torch.cuda.synchronize()
+    assert torch.equal(clean.view(torch.int16), poisoned.view(torch.int16))

@@ -573,6 +573,7 @@ template <int KT, int D, int HPW, int NBUF>
 struct ValuWorker {
   static constexpr int kLdsPerWave = 0;
   static constexpr long long kEvenXcdShare = 1120;
+  static constexpr bool kPace = false;
   static __device__ __forceinline__ int heads_per_wave(int /*ratio*/) { return HPW; }
   struct Pre {};  // (this flavour issues its first requests inside attend)
   static __device__ __forceinline__ void prefetch(const PagedLaunch&, int, int, int, int, int,
@@ -580,7 +581,8 @@ struct ValuWorker {
   static __device__ __forceinline__ void unit(const PagedLaunch& a, int lane, unsigned char* /*lds*/,
                                               int b, int g, int h0, int j_begin, int j_end,
                                               int t_start, int t_end, bool fused, bool write_new,
-                                              size_t slot0, size_t P, const Pre&, int) {
+                                              size_t slot0, size_t P, const Pre&, int,
+                                              int* = nullptr, const int* = nullptr) {
     HeadState<HPW, D / 8> st;
     attend<KT, D, HPW, NBUF>(a, lane, b, g, h0, j_begin, j_end, t_start, t_end, st, fused,
                              write_new);
@@ -849,6 +851,13 @@ struct MfmaWorker {
   using S = MShape<KT, D>;
   static constexpr int kLdsPerWave = 16 * S::ROWB;
   static constexpr long long kEvenXcdShare = 1060;
+  // The two waves on one SIMD keep pace (see unit): by default the older
+  // one takes the issue slots and finishes its share long before the other,
+  // which then streams alone for the rest of the launch; with one-byte
+  // caches, whose blocks are half the bytes, that half of the launch ran
+  // short of loads in flight (the GQA batch over INT8 codes: 124.4 -> 119.6
+  // us with pacing, HIP events; bf16 blocks: 217 -> 219 us, so not there).
+  static constexpr bool kPace = KT != kBF16;
   static __device__ __forceinline__ int heads_per_wave(int ratio) { return ratio < 16 ? ratio : 16; }
 
   static __device__ __forceinline__ void write(const PagedLaunch& a, int lane, size_t slot0,
@@ -965,10 +974,14 @@ struct MfmaWorker {
   // taken from k_new / v_new as a one-token block after the others, and with
   // `write_new` the wave also stores head g's part of those rows into their
   // cache slot.  `pr` holds this unit's prefetch for blocks j_pre .. +63.
+  // With `pace` (this wave's count of blocks done, in LDS) and `sibling`
+  // (that of the other wave on its SIMD), a wave more than one block ahead
+  // of its sibling lowers its issue priority until the sibling catches up.
   static __device__ __forceinline__ void unit(const PagedLaunch& a, int lane, unsigned char* lds,
                                               int b, int g, int h0, int j_begin, int j_end,
                                               int t_start, int t_end, bool fused, bool write_new,
-                                              size_t slot0, size_t P, const Pre& pr, int j_pre) {
+                                              size_t slot0, size_t P, const Pre& pr, int j_pre,
+                                              int* pace = nullptr, const int* sibling = nullptr) {
     const int ratio = a.num_q_heads / a.num_kv_heads;
     const int nheads = heads_per_wave(ratio);
     const int G = lane >> 4, i = lane & 15;
@@ -1018,6 +1031,14 @@ struct MfmaWorker {
             block_of(jj, nv);
             mfma_block<KT, D>(buf[s0], q, qb, lds, lane,
                               max(0, t_start - (c0 + jj) * kBlockTokens), nv, sl2, st);
+            if (pace) {
+              const int done = *pace + 1;
+              *pace = done;
+              if (done > *sibling + 1)
+                __builtin_amdgcn_s_setprio(0);
+              else
+                __builtin_amdgcn_s_setprio(2);
+            }
           }
           int nv;
           const int blk = block_of(jj + NBUF, nv);
@@ -1139,6 +1160,10 @@ void paged_balanced_kernel(PagedLaunch a) {
   // non-empty sequences before b, then [batch] lengths clamped to
   // max_seq_len.
   extern __shared__ int blk_prefix[];
+  // Blocks done by each wave (pacing of the two waves on a SIMD, wave w and
+  // w ^ 4 of an eight-wave workgroup).
+  __shared__ int pace[WG];
+  if ((threadIdx.x & (kWave - 1)) == 0) pace[threadIdx.x >> 6] = 0;
   int* const seq_prefix = blk_prefix + a.batch + 1;
   int* const len_of = seq_prefix + a.batch + 1;
   const int lane = threadIdx.x & (kWave - 1);
@@ -1264,8 +1289,10 @@ void paged_balanced_kernel(PagedLaunch a) {
       const int first = owner(vpos(b, ug, nb, 0));
       const int piece = wg - first;
       const size_t row0 = static_cast<size_t>(b) * a.num_q_heads + h0;
+      constexpr bool kPaced = W::kPace && WG == 8;
       W::unit(a, lane, lds, b, g, h0, js + j0, js + j0 + (seg_end - item), t_start, t_end, fused,
-              hc == 0, row0 * P + piece, P, pr, js + j0);
+              hc == 0, row0 * P + piece, P, pr, js + j0, kPaced ? &pace[wave] : nullptr,
+              kPaced ? &pace[wave ^ 4] : nullptr);
       if (piece == 0 && lane < hpw)
         a.counts[row0 + lane] = owner(vpos(b, ug, nb, nb - 1)) - first + 1;
     }

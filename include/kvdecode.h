@@ -372,9 +372,12 @@ int kvd_lds_read(int mode, int groups, int iters, void* cycles, void* sink, size
  *   out[b][h] = sum_t softmax(z)_t c_t  (latent space, width d_c)
  * The caller chooses `scale` (the Python binding defaults to 1/sqrt(d_c/4 +
  * d_rope), the per-head width of the un-absorbed key when d_c = 4 d_h).
- * Both products run on bf16 MFMA with fp32 accumulation.  Each softmax
- * weight enters the value product as a bf16 value plus its bf16 remainder
- * (about 16 bits of the weight); the weight sum takes the fp32 weights.
+ * Both products run on MFMA with fp32 accumulation: the scores on bf16, the
+ * value product on fp16, each softmax weight rounded to fp16 (11 bits) and
+ * the latent values converted from bf16 (exact for magnitudes in [2^-14,
+ * 65504], smaller ones off by at most 2^-25; latent values beyond 65504
+ * overflow and the output holds inf/NaN).  The weight sum takes the fp32
+ * weights.
  *
  *   out      [batch, num_q_heads, d_c] bf16
  *   q        [batch, num_q_heads, d_c + d_rope] bf16

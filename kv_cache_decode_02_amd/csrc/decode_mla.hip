@@ -8,7 +8,9 @@
 // ("KV Cache（键值缓存）", 2.2 路线一, the MLA equations and the decoupled-RoPE
 // note; 4 实现要点, MLA needs a kernel that absorbs the up-projection).
 // 128 heads against one shared row is a dense contraction, so both products
-// run on MFMA 32x32x16 (bf16 operands, fp32 accumulation).
+// run on MFMA 32x32x16 with fp32 accumulation: the scores on the bf16 rows
+// and queries, the value product on fp16 (weights, and the latent columns
+// converted from bf16, which is exact in fp16's range).
 //
 // Work decomposition:
 //   workgroup = (sequence b, partition p, group of 64 query heads), 8 waves,
@@ -33,14 +35,15 @@
 //            wave, 36 MFMAs; every lane ends with one head and 16 tokens.
 //   Softmax: online per head with a lazily raised reference max (raised only
 //            when a score exceeds it by more than kRaise log2 units); the
-//            weights enter the value MFMA as a bf16 value plus its bf16
-//            remainder, the running sum takes them in fp32.
+//            weights enter the value MFMA rounded to fp16, the running sum
+//            takes them in fp32.
 //   Output:  O^T[32 x 32] += C_tile^T[32 x 32] . P^T[32 x 32] per column
-//            tile, token half and head block, twice (value, remainder); the
-//            A operand (one latent column per lane, tokens along K) is read
-//            from the token-major tile with LDS transpose loads and feeds the
-//            MFMAs of both head blocks, and each lane's accumulator column is
-//            its own head, so rescaling needs no data movement between lanes.
+//            tile, token half and head block (fp16 MFMA); the A operand (one
+//            latent column per lane, tokens along K) is read from the
+//            token-major tile with LDS transpose loads, converted to fp16 and
+//            feeds the MFMAs of both head blocks, and each lane's accumulator
+//            column is its own head, so rescaling needs no data movement
+//            between lanes.
 //   Pipeline: step t computes the scores and weights of tile t and the value
 //   product of tile t - 1, and stages tile t + 1, with one barrier per step;
 //   the weights and rescale factors alternate between two LDS buffers.
@@ -94,6 +97,21 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+
+__device__ __forceinline__ f32x16_t mfma32_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight bf16 values (four words) as eight fp16 values: exact for magnitudes
+// in [2^-14, 65504], the smaller ones rounded to fp16 subnormals (absolute
+// error <= 2^-25), the larger ones infinite.
+__device__ __forceinline__ f16x8_t bf16x8_to_f16(uint4 u) {
+  const uint4 h = make_uint4(pack_f16x2(bf16_lo(u.x), bf16_hi(u.x)), pack_f16x2(bf16_lo(u.y), bf16_hi(u.y)),
+                             pack_f16x2(bf16_lo(u.z), bf16_hi(u.z)), pack_f16x2(bf16_lo(u.w), bf16_hi(u.w)));
+  return __builtin_bit_cast(f16x8_t, h);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // x, as a value the compiler must take to change at this point: addresses
@@ -134,8 +152,8 @@ struct MlaLaunchDev {
 
 struct MlaShared {
   uint8_t tiles[kStages][kTileBytes];
-  // Weights of the tile [step parity][head block][token half][value, remainder][lane]
-  uint4 pw[2][2][2][2][kWave];
+  // fp16 weights of the tile [step parity][head block][token half][lane]
+  uint4 pw[2][2][2][kWave];
   float alpha[2][2][kBlockHeads];  // rescale of the step [step parity][head block][head]
 };
 
@@ -288,23 +306,20 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       }
       if (g == 0) sh.alpha[par][hb][r32] = al;
       // Weights of token half th (registers 8 th .. 8 th + 7, the K-slots of
-      // the value product's K-step th): a bf16 value and its bf16 remainder
-      // (about 16 bits of weight: 8-bit weights move outputs that cancel over
-      // a few positions by ~1e-3); the sum takes the fp32 weights.
+      // the value product's K-step th), rounded to fp16 (11 bits: 8-bit
+      // weights move outputs that cancel over a few positions by ~1e-3); the
+      // sum takes the fp32 weights.
 #pragma unroll
       for (int th = 0; th < 2; ++th) {
-        uint32_t hi[4], lo[4];
+        uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p0 = exp2_fast(z[8 * th + 2 * e] - m_run);
           const float p1 = exp2_fast(z[8 * th + 2 * e + 1] - m_run);
           l_half += p0 + p1;
-          const uint32_t w = opaque(pack_bf16x2(p0, p1));
-          hi[e] = w;
-          lo[e] = pack_bf16x2(p0 - bf16_lo(w), p1 - bf16_hi(w));
+          w[e] = pack_f16x2(p0, p1);
         }
-        sh.pw[par][hb][th][0][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        sh.pw[par][hb][th][1][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        sh.pw[par][hb][th][lane] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     };
 
@@ -433,13 +448,11 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       if (!active0 || t < 1 || t > ntiles) return;
       const int par = (t - 1) & 1;
       const float al0 = sh.alpha[par][0][r32], al1 = sh.alpha[par][1][r32];
-      uint4 pv[2][2][2];  // weights of the tile: [head block][token half][value, remainder]
+      uint4 pv[2][2];  // fp16 weights of the tile: [head block][token half]
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int vr = 0; vr < 2; ++vr) pv[h][j][vr] = sh.pw[par][h][j][vr][lane];
+        for (int j = 0; j < 2; ++j) pv[h][j] = sh.pw[par][h][j][lane];
       if (__builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f)) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -465,21 +478,19 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const uint2 w0 = w[ct][j][0], w1 = w[ct][j][1];
-          const bf16x8_t va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+          const f16x8_t va = bf16x8_to_f16(make_uint4(w0.x, w0.y, w1.x, w1.y));
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            acc[h][ct] = mfma32(va, as_bf16x8(pv[h][j][0]), acc[h][ct]);
-            acc[h][ct] = mfma32(va, as_bf16x8(pv[h][j][1]), acc[h][ct]);
-          }
+          for (int h = 0; h < 2; ++h)
+            acc[h][ct] = mfma32_f16(va, __builtin_bit_cast(f16x8_t, pv[h][j]), acc[h][ct]);
         }
       constexpr int frags = 2 * NCT;
       KVD_SCHED_GROUP(kSchedDsRead, 2 * kPvAhead);
 #pragma unroll
       for (int f = 0; f < frags - kPvAhead; ++f) {
-        KVD_SCHED_GROUP(kSchedMfma, 4);
+        KVD_SCHED_GROUP(kSchedMfma, 2);
         KVD_SCHED_GROUP(kSchedDsRead, 2);
       }
-      KVD_SCHED_GROUP(kSchedMfma, 4 * kPvAhead);
+      KVD_SCHED_GROUP(kSchedMfma, 2 * kPvAhead);
     };
 
     // Waves 2-5 stage first, so that the products of waves 4-5 reach the

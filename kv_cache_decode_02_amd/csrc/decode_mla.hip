@@ -21,10 +21,11 @@
 //     value waves 2-7   (a range of 32-column tiles of the latent, both head
 //                       blocks): the unnormalised output of 64 heads x their
 //                       columns in registers, fed by those weights.  Wave w
-//                       runs beside wave w + 4 on a SIMD; waves 2-5 take
-//                       three column tiles and 6-7 two, which with the order
-//                       of each wave's staging and products balances the
-//                       SIMDs' matrix units over a tile.
+//                       runs beside wave w + 4 on a SIMD; waves 4-5 (beside
+//                       the score waves) take two column tiles and the
+//                       others three, which with the order of each wave's
+//                       staging and products balances the SIMDs over a
+//                       tile.
 //   Tokens come in tiles of 32 (two 16-token blocks), loaded once per
 //   workgroup through the block table (rows past the sequence end read as
 //   zeros) by the value waves, stored token-major in LDS and read by all 8
@@ -87,9 +88,9 @@ static_assert(kBlockTokens * kRowBytes == kStageLanes * kLoadChunks * 16, "tile 
 
 // Column tiles of value wave w (2 .. 7): [first, first + count).
 __device__ __forceinline__ int value_first_tile(int w) {
-  return w == 2 ? 0 : w == 3 ? 3 : w == 4 ? 6 : w == 5 ? 9 : w == 6 ? 12 : 14;
+  return w == 2 ? 0 : w == 3 ? 3 : w == 4 ? 6 : w == 5 ? 8 : w == 6 ? 10 : 13;
 }
-__device__ __forceinline__ int value_tile_count(int w) { return (w == 6 || w == 7) ? 2 : 3; }
+__device__ __forceinline__ int value_tile_count(int w) { return (w == 4 || w == 5) ? 2 : 3; }
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
@@ -356,8 +357,9 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
   // 4 g + r % 4 in register r.
   // (The whole value path, staging included, is instantiated once per column
   // tile count, so that no register of one instance lives across the other.)
-  auto run = [&](auto nct_c) __attribute__((always_inline)) {
+  auto run = [&](auto nct_c, auto stage_first_c) __attribute__((always_inline)) {
     constexpr int NCT = decltype(nct_c)::value;
+    constexpr bool kStageFirst = decltype(stage_first_c)::value;
     // ---- Value waves: staging of the tiles, then the value products.
     // Tile loads: waves 2-4 fetch the tile's first 16-token block, waves 5-7
     // the second (a block is 16 x 1152 contiguous bytes), each lane 6 chunks of
@@ -495,16 +497,15 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
 
     // Waves 2-5 stage first, so that the products of waves 4-5 reach the
     // matrix unit after the score MFMA chain beside them has started; waves
-    // 6-7 (two column tiles) run their products first, while waves 2-3 on
-    // their SIMDs stage.
+    // 6-7 run their products first, while waves 2-3 on their SIMDs stage.
     for (int t = 0; t < nsteps; t += 2) {
-      if constexpr (NCT == 2) step(t);
+      if constexpr (!kStageFirst) step(t);
       stage(t, pre[1]);
-      if constexpr (NCT != 2) step(t);
+      if constexpr (kStageFirst) step(t);
       __syncthreads();
-      if constexpr (NCT == 2) step(t + 1);
+      if constexpr (!kStageFirst) step(t + 1);
       stage(t + 1, pre[0]);
-      if constexpr (NCT != 2) step(t + 1);
+      if constexpr (kStageFirst) step(t + 1);
       __syncthreads();
     }
     if (!active0) return;
@@ -523,8 +524,9 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
                           acc[h][ct][4 * qd + 3]);
     }
   };
-  if (value_tile_count(wave) == 2) run(std::integral_constant<int, 2>{});
-  else run(std::integral_constant<int, 3>{});
+  if (wave >= 6) run(std::integral_constant<int, 3>{}, std::false_type{});
+  else if (value_tile_count(wave) == 2) run(std::integral_constant<int, 2>{}, std::true_type{});
+  else run(std::integral_constant<int, 3>{}, std::true_type{});
 }
 
 }  // namespace

@@ -377,7 +377,8 @@ int kvd_lds_read(int mode, int groups, int iters, void* cycles, void* sink, size
  * the latent values converted from bf16 (exact for magnitudes in [2^-14,
  * 65504], smaller ones off by at most 2^-25; latent values beyond 65504
  * overflow and the output holds inf/NaN).  The weight sum takes the fp32
- * weights.
+ * weights.  Each partition's partial row is kept in the workspace divided by
+ * its weight sum, in fp16 (its magnitudes are at most the latent values').
  *
  *   out      [batch, num_q_heads, d_c] bf16
  *   q        [batch, num_q_heads, d_c + d_rope] bf16

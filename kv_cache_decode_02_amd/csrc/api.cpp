@@ -148,7 +148,8 @@ WorkspaceLayout workspace_layout(int batch, int num_q_heads, int num_partitions,
                                  bool balanced) {
   WorkspaceLayout w;
   const size_t slots = static_cast<size_t>(batch) * num_q_heads * num_partitions;
-  w.o_bytes = slots * head_dim * sizeof(float);
+  // The latent (MLA) path stores its rows normalised, in fp16.
+  w.o_bytes = slots * head_dim * (head_dim == kLatentWidth ? sizeof(uint16_t) : sizeof(float));
   w.ml_offset = align256(w.o_bytes);
   w.counts_offset = w.ml_offset + align256(slots * 2 * sizeof(float));
   const size_t counts = balanced ? static_cast<size_t>(batch) * num_q_heads * sizeof(int32_t) : 0;

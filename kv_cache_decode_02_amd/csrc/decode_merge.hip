@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
   int np = len <= 0 ? 0 : a.counts ? a.counts[bh] : (len + a.partition_tokens - 1) / a.partition_tokens;
   np = min(max(np, 0), static_cast<int>(P));
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + bh * P;
-  const float* o = a.ws_o + bh * P * D;
+  // (fp16 rows for the latent width: a float pointer to their halves)
+  const float* o = a.ws_o + bh * P * (kF16Rows<D> ? D / 2 : D);
 
   const bool active = lane * DL < D;
   if constexpr (WPB == 1) {
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
     const float2 v = p0 + lane < np ? ml[p0 + lane] : make_float2(kMinusBig, 0.f);
     const float w_lane = v.y > 0.f ? exp2_fast(v.x - M) : 0.f;
     den += w_lane * v.y;
+    const float wr_lane = kF16Rows<D> ? w_lane * v.y : w_lane;  // weight of the lane's row
     uint64_t mask = __builtin_amdgcn_ballot_w64(v.y > 0.f);
     while (mask) {
       int idx[kRows];
@@ -79,12 +81,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeLaunch a) {
       float rows[kRows][DL];
 #pragma unroll
       for (int k = 0; k < kRows; ++k)
-#pragma unroll
-        for (int d = 0; d < DL; ++d)
-          rows[k][d] = (idx[k] >= 0 && active) ? o[(p0 + idx[k]) * D + lane * DL + d] : 0.f;
+        load_piece_row<D, DL>(rows[k], o, p0 + max(idx[k], 0), lane, idx[k] >= 0 && active);
 #pragma unroll
       for (int k = 0; k < kRows; ++k) {
-        const float w = __shfl(w_lane, idx[k] >= 0 ? idx[k] : 0, kWave);
+        const float w = __shfl(wr_lane, idx[k] >= 0 ? idx[k] : 0, kWave);
         if (idx[k] >= 0) {
 #pragma unroll
           for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);

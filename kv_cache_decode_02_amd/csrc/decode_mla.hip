@@ -156,6 +156,7 @@ struct MlaShared {
   // fp16 weights of the tile [step parity][head block][token half][lane]
   uint4 pw[2][2][2][kWave];
   float alpha[2][2][kBlockHeads];  // rescale of the step [step parity][head block][head]
+  float lsum[2][kBlockHeads];      // weight sum of each head at the end
 };
 
 __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) {
@@ -339,6 +340,10 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       const size_t ws_slot = (static_cast<size_t>(b) * a.num_heads + head) * P + p;
       reinterpret_cast<float2*>(a.ws_ml)[ws_slot] = make_float2(m_run, l);
     }
+    // The value waves divide their sums by it (one barrier, which every wave
+    // of the workgroup reaches).
+    if (g == 0) sh.lsum[hb][r32] = active && head_ok ? l : 0.f;
+    __syncthreads();
     return;
   }
 
@@ -508,20 +513,25 @@ __global__ __launch_bounds__(kThreads) void mla_partials_kernel(MlaLaunchDev a) 
       if constexpr (kStageFirst) step(t + 1);
       __syncthreads();
     }
+    __syncthreads();  // the score waves' weight sums
     if (!active0) return;
+    // The piece's row divided by its weight sum, in fp16 (its magnitude is at
+    // most that of the largest latent value).
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int head = head0 + h * kBlockHeads + r32;
       if (head >= a.num_heads) continue;
+      const float l = sh.lsum[h][r32];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
       const size_t ws_slot = (static_cast<size_t>(b) * a.num_heads + head) * P + p;
-      float* orow = a.ws_o + ws_slot * kDc + 32 * ct0 + 4 * g;
+      _Float16* orow = reinterpret_cast<_Float16*>(a.ws_o) + ws_slot * kDc + 32 * ct0 + 4 * g;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<float4*>(orow + 32 * ct + 8 * qd) =
-              make_float4(acc[h][ct][4 * qd], acc[h][ct][4 * qd + 1], acc[h][ct][4 * qd + 2],
-                          acc[h][ct][4 * qd + 3]);
+          *reinterpret_cast<uint2*>(orow + 32 * ct + 8 * qd) =
+              make_uint2(pack_f16x2(acc[h][ct][4 * qd] * inv, acc[h][ct][4 * qd + 1] * inv),
+                         pack_f16x2(acc[h][ct][4 * qd + 2] * inv, acc[h][ct][4 * qd + 3] * inv));
     }
   };
   if (wave >= 6) run(std::integral_constant<int, 3>{}, std::false_type{});

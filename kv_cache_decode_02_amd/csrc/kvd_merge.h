@@ -48,6 +48,37 @@ __device__ __forceinline__ void load_row(float (&dst)[DL], const float* src, boo
   }
 }
 
+// Rows of a piece: unnormalised fp32 sums (paged path), or for the latent
+// width the sums divided by the piece's weight sum l, in fp16 (MLA path).
+template <int D>
+constexpr bool kF16Rows = D == 512;
+
+// Row `row` of the pieces at `o` (for fp16 rows `o` addresses halves), the
+// lane's DL dims, or zeros without `take`.
+template <int D, int DL>
+__device__ __forceinline__ void load_piece_row(float (&dst)[DL], const float* o, int row, int lane,
+                                               bool take) {
+  if constexpr (kF16Rows<D>) {
+    static_assert(DL == 8, "fp16 rows: 16 bytes per lane");
+    if (take) {
+      const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(o) +
+                                                      static_cast<size_t>(row) * D + lane * DL);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, w[k]);
+        dst[2 * k] = static_cast<float>(h[0]);
+        dst[2 * k + 1] = static_cast<float>(h[1]);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < DL; ++d) dst[d] = 0.f;
+    }
+  } else {
+    load_row<DL>(dst, o + static_cast<size_t>(row) * D + lane * DL, take);
+  }
+}
+
 // One wave combines pieces [0, np) of one (b, h): `ml` holds their (m, l)
 // pairs and `o` their rows of D floats.  On return lane `lane` holds dims
 // lane * DL .. of the unnormalised sum and every lane the denominator.
@@ -63,19 +94,20 @@ __device__ __forceinline__ void merge_pieces(const float2* ml, const float* o, i
     const float2 v = lane < np ? ml[lane] : make_float2(kMinusBig, 0.f);
     float rows[kRows][DL];
 #pragma unroll
-    for (int k = 0; k < kRows; ++k) load_row<DL>(rows[k], o + k * D + lane * DL, k < np && active);
+    for (int k = 0; k < kRows; ++k) load_piece_row<D, DL>(rows[k], o, k, lane, k < np && active);
     float M = v.y > 0.f ? v.x : kMinusBig;
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, shfl_xor_f(M, s));
     const float w_lane = v.y > 0.f ? exp2_fast(v.x - M) : 0.f;
     den = w_lane * v.y;
+    const float wr_lane = kF16Rows<D> ? w_lane * v.y : w_lane;  // weight of the lane's row
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) den += shfl_xor_f(den, s);
     // (An empty piece, weight 0, may hold no row values at all: it is
     // skipped rather than multiplied by 0.)
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
-      const float w = __shfl(w_lane, k, kWave);
+      const float w = __shfl(wr_lane, k, kWave);
       if (w != 0.f) {
 #pragma unroll
         for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);
@@ -98,6 +130,7 @@ __device__ __forceinline__ void merge_pieces(const float2* ml, const float* o, i
     const float2 v = p0 + lane < np ? ml[p0 + lane] : make_float2(kMinusBig, 0.f);
     const float w_lane = v.y > 0.f ? exp2_fast(v.x - M) : 0.f;
     den += w_lane * v.y;
+    const float wr_lane = kF16Rows<D> ? w_lane * v.y : w_lane;
     uint64_t mask = __builtin_amdgcn_ballot_w64(v.y > 0.f);
     while (mask) {
       int idx[kRows];
@@ -109,10 +142,10 @@ __device__ __forceinline__ void merge_pieces(const float2* ml, const float* o, i
       float rows[kRows][DL];
 #pragma unroll
       for (int k = 0; k < kRows; ++k)
-        load_row<DL>(rows[k], o + (p0 + max(idx[k], 0)) * D + lane * DL, idx[k] >= 0 && active);
+        load_piece_row<D, DL>(rows[k], o, p0 + max(idx[k], 0), lane, idx[k] >= 0 && active);
 #pragma unroll
       for (int k = 0; k < kRows; ++k) {
-        const float w = __shfl(w_lane, idx[k] >= 0 ? idx[k] : 0, kWave);
+        const float w = __shfl(wr_lane, idx[k] >= 0 ? idx[k] : 0, kWave);
         if (idx[k] >= 0) {
 #pragma unroll
           for (int d = 0; d < DL; ++d) acc[d] = fmaf(w, rows[k][d], acc[d]);
